@@ -1,0 +1,128 @@
+"""Seeded synthetic inputs shared by the oracle checks and the HIP path.
+
+This module holds none of attention's arithmetic: it only draws i.i.d.
+N(0, 1) tensors (the pages' own benchmark draws its Q, K, V with randn at
+shape (1, 12, 2048, 64): ijyty.com/news/1153309, "Flash Attention 技术原理让
+Transformer 更快更高效", section "性能对比"), rounds them to the storage dtype
+with round-to-nearest-even, and picks seeded subsets of rows to check.  The
+oracle reads the rounded values upcast to float64, so parity measures the
+kernel's error, not input quantisation.
+
+Recipe: workload k uses seed k; tensor t in {Q: 0, K: 1, V: 2, dO: 3} is
+numpy.random.default_rng([k, t]).standard_normal(shape, dtype=float32),
+times the workload's input multiplier, then rounded to the dtype.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    B: int
+    H: int
+    N: int
+    D: int
+    dtype: str          # "f32", "bf16" or "f16"
+    causal: bool
+    backward: bool
+    input_mult: float = 1.0
+    check_rows: int = 0  # 0: check every row; else a seeded subset of rows
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.N, self.D)
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.D)
+
+
+# The five workloads of the attention path (shape, dtype, mask, passes).
+WORKLOADS = {
+    "c1": Workload("fwd_f32_b1h1n256d64", 1, 1, 1, 256, 64, "f32", False, False),
+    "c2": Workload("fwd_bf16_b1h12n2048d64", 2, 1, 12, 2048, 64, "bf16", False, False),
+    "c3": Workload("train_causal_bf16_b8h12n1024d64", 3, 8, 12, 1024, 64, "bf16", True, True),
+    "c4": Workload("fwd_bf16_b1h16n16384d128_x0.5", 4, 1, 16, 16384, 128, "bf16", False, False,
+                   input_mult=0.5, check_rows=256),
+    "c5": Workload("train_causal_bf16_b1h16n65536d64", 5, 1, 16, 65536, 64, "bf16", True, True,
+                   check_rows=128),
+}
+
+
+def round_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round-to-nearest-even.
+    Inputs are finite (N(0,1) draws), so no NaN handling is needed."""
+    x32 = np.ascontiguousarray(x32, dtype=np.float32)
+    u = x32.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def round_to_dtype(x32: np.ndarray, dtype: str):
+    """Returns (values as float32, raw storage array for upload)."""
+    if dtype == "f32":
+        x = np.ascontiguousarray(x32, dtype=np.float32)
+        return x, x
+    if dtype == "bf16":
+        bits = round_bf16_bits(x32)
+        return bf16_bits_to_f32(bits), bits
+    if dtype == "f16":
+        h = x32.astype(np.float16)  # numpy's float32->float16 cast is RNE
+        return h.astype(np.float32), h
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def draw(seed: int, tensor: str, shape, dtype: str, mult: float = 1.0):
+    """One seeded tensor: (float32 values, raw storage array)."""
+    rng = np.random.default_rng([seed, TENSOR_IDS[tensor]])
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if mult != 1.0:
+        x = x * np.float32(mult)
+    return round_to_dtype(x, dtype)
+
+
+def make_inputs(w: Workload, with_grad=None):
+    """Dict name -> (float32 values, raw storage) for q, k, v (and do)."""
+    names = ["q", "k", "v"]
+    if with_grad if with_grad is not None else w.backward:
+        names.append("do")
+    return {n: draw(w.seed, n, w.shape, w.dtype, w.input_mult if n != "do" else 1.0)
+            for n in names}
+
+
+def check_row_subset(w: Workload, count: int = None, seed_offset: int = 1000):
+    """Seeded (b, h, i) triples to check at full size.
+
+    Always holds i in {0, 1, 63, 64, 127, 128, N/2, N-1} (tile edges and the
+    causal diagonal) in the first and last head of batch 0; the rest are drawn
+    uniformly without replacement from default_rng(seed + seed_offset).
+    """
+    count = count or w.check_rows
+    N = w.N
+    fixed = sorted({i for i in (0, 1, 63, 64, 127, 128, N // 2, N - 1) if 0 <= i < N})
+    picked = []
+    for h in sorted({0, w.H - 1}):
+        picked += [(0, h, i) for i in fixed]
+    seen = set(picked)
+    rng = np.random.default_rng(w.seed + seed_offset)
+    total = w.B * w.H * N
+    while len(picked) < count:
+        flat = int(rng.integers(total))
+        b, rem = divmod(flat, w.H * N)
+        h, i = divmod(rem, N)
+        if (b, h, i) not in seen:
+            seen.add((b, h, i))
+            picked.append((b, h, i))
+    return np.array(picked, dtype=np.int64)
