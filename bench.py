@@ -1,0 +1,249 @@
+#!/usr/bin/env python
+"""Attention forward + backward throughput on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+fa_fwd (O and LSE, online softmax, causal tile skipping) followed by fa_bwd
+(Delta, dK/dV and dQ kernels with on-chip recomputation).  The default
+workload is the long-context causal training problem B=1, H=16, N=65536,
+D=64, bf16, seeded i.i.d. N(0, 1) inputs already resident in HBM.
+
+Prints ONE JSON line.  ``value`` is algorithmic TFLOP/s of the step:
+forward 4*B*H*N^2*D and backward 10*B*H*N^2*D, both halved under the causal
+mask, divided by the step time measured with HIP events on the launch stream.
+The ``roofline`` object covers the kernel that takes the most time; its
+duration comes from per-launch HIP events recorded by the library on the
+same stream during the timed steps.  ``cpu_baseline`` times the float64
+oracle on a bounded sample (the leading R x R causal block of head 0) on
+the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s on 1 MI355X and % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def flops(w):
+    f = 4.0 * w.B * w.H * w.N * w.N * w.D
+    b = 10.0 * w.B * w.H * w.N * w.N * w.D if w.backward else 0.0
+    if w.causal:
+        f, b = f / 2, b / 2
+    return f, b
+
+
+def kernel_algorithmic(w):
+    """Algorithmic work of one launch of each kernel.  Contractions count
+    2*N^2*D per head (halved when causal); the dQ kernel is credited with
+    dQ = dS K only (its recomputation of S and dP is not algorithmic work);
+    Delta is credited with its bytes (read O, dO; write Delta)."""
+    unit = 2.0 * w.B * w.H * w.N * w.N * w.D * (0.5 if w.causal else 1.0)
+    el = 2 if w.dtype in ("bf16", "f16") else 4
+    return {
+        "fwd": ("mfma", 2 * unit),           # S = Q K^T, O = P V
+        "bwd_delta": ("hbm", 2.0 * w.B * w.H * w.N * w.D * el + 4.0 * w.B * w.H * w.N),
+        "bwd_dkdv": ("mfma", 4 * unit),      # S, dP, dV, dK
+        "bwd_dq": ("mfma", 1 * unit),        # dQ
+    }
+
+
+def upload(raw, dtype):
+    import numpy as np
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(raw)).cuda()
+
+
+def run_gpu(w, steps, warmup):
+    import torch
+    from exact_io_aware_58_amd import fa, inputs
+
+    log(f"[bench] inputs {w.name} {w.shape} {w.dtype} causal={w.causal}")
+    devs = {n: upload(raw, w.dtype) for n, (_, raw) in inputs.make_inputs(w).items()}
+    q, k, v = devs["q"], devs["k"], devs["v"]
+    code = {"f32": fa.FA_F32, "bf16": fa.FA_BF16, "f16": fa.FA_F16}[w.dtype]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+    if w.backward:
+        do = devs["do"]
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        wsb = fa.fa_bwd_workspace_bytes(code, w.B, w.H, w.N, w.D, w.causal)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    args_f = (code, w.B, w.H, w.N, w.D, w.scale, w.causal, q.data_ptr(), k.data_ptr(),
+              v.data_ptr(), o.data_ptr(), lse.data_ptr(), sh)
+    if w.backward:
+        args_b = (code, w.B, w.H, w.N, w.D, w.scale, w.causal, q.data_ptr(), k.data_ptr(),
+                  v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                  dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), wsb, sh)
+
+    def step():
+        rc = fa.fa_fwd(*args_f)
+        if rc != fa.FA_OK:
+            raise fa.FAError(rc, "fa_fwd")
+        if w.backward:
+            rc = fa.fa_bwd(*args_b)
+            if rc != fa.FA_OK:
+                raise fa.FAError(rc, "fa_bwd")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {warmup} done; timing {steps} steps")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fa.fa_timing_enable(True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    kernels = {}
+    for kid in range(fa.FA_KERNEL_COUNT):
+        n, ms, dropped = fa.fa_timing_read(kid)
+        if n:
+            kernels[fa.fa_kernel_name(kid)] = {"launches": n, "avg_ms": ms / n}
+    fa.fa_timing_enable(False)
+    log(f"[bench] {steps} steps in {total_ms:.3f} ms")
+    return total_ms / steps, kernels
+
+
+def cpu_baseline(w, rows):
+    """The float64 oracle on the leading rows x rows block of head 0 (causal:
+    those queries see only those keys, so the block is a self-contained slice
+    of the workload), forward + backward."""
+    import numpy as np
+    import oracle
+    from exact_io_aware_58_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = 1
+    rows = min(rows, w.N)
+    t = {}
+    for name in ("q", "k", "v", "do"):
+        x, _ = inputs.draw(w.seed, name, w.shape, w.dtype, w.input_mult if name != "do" else 1.0)
+        t[name] = x[:1, :1, :rows].astype(np.float64)
+    log(f"[bench] cpu baseline: oracle on head 0, rows [0, {rows}) ...")
+    t0 = time.perf_counter()
+    oracle.attention_fwd(t["q"], t["k"], t["v"], w.scale, w.causal)
+    if w.backward:
+        oracle.attention_bwd(t["q"], t["k"], t["v"], t["do"], w.scale, w.causal)
+    sec = time.perf_counter() - t0
+    sub = type(w)(w.name, w.seed, 1, 1, rows, w.D, w.dtype, w.causal, w.backward)
+    f, b = flops(sub)
+    return {
+        "value": (f + b) / sec / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"head 0 of batch 0, leading {rows}x{rows} "
+                  f"{'causal ' if w.causal else ''}block, "
+                  f"{'fwd+bwd' if w.backward else 'fwd'} in float64 ({sec:.1f} s)",
+        "seconds": sec,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c5", help="c1..c5 (default c5)")
+    ap.add_argument("--cpu-rows", type=int, default=16384,
+                    help="rows of the oracle sample timed for cpu_baseline (0: skip)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the N=16384 D=128 forward-only figure")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the attention path is built and timed on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    from exact_io_aware_58_amd import inputs
+    w = inputs.WORKLOADS[args.workload]
+    ms, kernels = run_gpu(w, args.steps, args.warmup)
+    f, b = flops(w)
+    value = (f + b) / (ms / 1e3) / 1e12
+
+    alg = kernel_algorithmic(w)
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
+    bound, work = alg[dom]
+    dur = kernels[dom]["avg_ms"] / 1e3
+    if bound == "mfma":
+        achieved, peak, unit = work / dur / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = work / dur / 1e9, PEAK_HBM_GBS, "GB/s"
+    for name, kv in kernels.items():
+        kb, kw = alg[name]
+        kv["achieved"] = kw / (kv["avg_ms"] / 1e3) / (1e12 if kb == "mfma" else 1e9)
+        kv["unit"] = "TFLOP/s" if kb == "mfma" else "GB/s"
+
+    passes = {}
+    if "fwd" in kernels:
+        passes["fwd"] = {"ms": kernels["fwd"]["avg_ms"],
+                         "tflops": f / (kernels["fwd"]["avg_ms"] / 1e3) / 1e12}
+    if w.backward:
+        bms = sum(kernels[k]["avg_ms"] for k in ("bwd_delta", "bwd_dkdv", "bwd_dq") if k in kernels)
+        passes["bwd"] = {"ms": bms, "tflops": b / (bms / 1e3) / 1e12}
+    for p in passes.values():
+        p["pct_of_bf16_peak"] = 100.0 * p["tflops"] / PEAK_BF16_TFLOPS
+
+    secondary = None
+    if not args.no_secondary and args.workload != "c4":
+        w4 = inputs.WORKLOADS["c4"]
+        ms4, k4 = run_gpu(w4, max(3, args.steps), args.warmup)
+        f4, _ = flops(w4)
+        secondary = {"workload": w4.name, "pass": "fwd", "ms": ms4,
+                     "tflops": f4 / (ms4 / 1e3) / 1e12,
+                     "pct_of_bf16_peak": 100.0 * f4 / (ms4 / 1e3) / 1e12 / PEAK_BF16_TFLOPS}
+
+    cpu = cpu_baseline(w, args.cpu_rows) if args.cpu_rows > 0 else None
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
+                   "causal": w.causal, "passes": "fwd+bwd" if w.backward else "fwd",
+                   "flops_per_step": f + b},
+        "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "passes": passes,
+        "kernels": kernels,
+        "roofline": {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak,
+                     "unit": unit, "frac": achieved / peak, "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    if secondary:
+        out["fwd_n16384_d128"] = secondary
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

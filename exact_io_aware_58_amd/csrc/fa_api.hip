@@ -1,0 +1,104 @@
+// fa_api.hip -- the C ABI of libfa.so (declared in include/fa.h): argument
+// validation, then kernel launches on the caller's stream.  Host-only code.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+constexpr int kMaxN = 1 << 24;
+
+bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shapes and scale; returns FA_OK or the status to report.
+int check_problem(int dtype, int B, int H, int N, int D, float scale) {
+  if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_UNSUPPORTED;
+  if (B <= 0 || H <= 0 || N <= 0 || N > kMaxN) return FA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  // element count and every launch's grid must fit the index types used
+  const double elems = (double)B * H * N * D;
+  if (elems > 9.0e18 / 4) return FA_ERR_INVALID_ARG;
+  const double tiles = (double)B * H * ((N + 63) / 64);
+  if (tiles > 2.0e9) return FA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+size_t delta_bytes(int B, int H, int N) {
+  size_t n = (size_t)B * H * N * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" int fa_version(void) { return 1; }
+
+extern "C" const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported dtype or head dimension";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int fa_fwd(int dtype, int B, int H, int N, int D, float scale, int causal,
+                      const void* Q, const void* K, const void* V, void* O, float* LSE,
+                      void* stream) {
+  int rc = check_problem(dtype, B, H, N, D, scale);
+  if (rc != FA_OK) return rc;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
+    return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a{dtype, B, H, N, D, scale, causal ? 1 : 0, Q, K, V, O, LSE,
+                (hipStream_t)stream};
+  hipError_t e;
+  {
+    fa::TimedLaunch t(FA_KERNEL_FWD, a.stream);
+    e = fa::launch_fwd(a);
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int D, int causal) {
+  (void)causal;
+  if (dtype == FA_F32 || check_problem(dtype, B, H, N, D, 1.f) != FA_OK) return 0;
+  return delta_bytes(B, H, N);
+}
+
+extern "C" int fa_bwd(int dtype, int B, int H, int N, int D, float scale, int causal,
+                      const void* Q, const void* K, const void* V, const void* O,
+                      const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_problem(dtype, B, H, N, D, scale);
+  if (rc != FA_OK) return rc;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;  // backward kernels are 16-bit only
+  const void* ptrs[] = {Q, K, V, O, dO, LSE, dQ, dK, dV};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < delta_bytes(B, H, N)) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
+  fa::BwdArgs a{dtype, B, H, N, D, scale, causal ? 1 : 0, Q, K, V, O, dO, LSE,
+                dQ, dK, dV, (float*)workspace, (hipStream_t)stream};
+  hipError_t e;
+  {
+    fa::TimedLaunch t(FA_KERNEL_BWD_DELTA, a.stream);
+    e = fa::launch_bwd_delta(a);
+  }
+  if (e != hipSuccess) return FA_ERR_HIP;
+  {
+    fa::TimedLaunch t(FA_KERNEL_BWD_DKDV, a.stream);
+    e = fa::launch_bwd_dkdv(a);
+  }
+  if (e != hipSuccess) return FA_ERR_HIP;
+  {
+    fa::TimedLaunch t(FA_KERNEL_BWD_DQ, a.stream);
+    e = fa::launch_bwd_dq(a);
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

@@ -1,0 +1,490 @@
+// fa_bwd.hip -- backward kernels with on-chip recomputation of S and P.
+//
+// Pages cited (by address and title):
+//   [csdn]      adg.csdn.net/6a311d0d10ee7a33f27dee1b.html
+//               "kk的大模型论文学习笔记 第8篇: FlashAttention"
+//   [guanweilu] guanweilu.cn/article/445.html
+//               "CUDA Kernel 级别的优化：Flash Attention 为什么比 PyTorch 原生实现快 5-10 倍"
+//
+// The pages' backward pass keeps no N x N matrix: it recomputes S and P on
+// chip when the gradients need them, because recomputing is cheaper than a
+// round trip through HBM ([csdn] "重计算：扔掉比存着更快"; [guanweilu]
+// "FlashAttention 的三板斧", third technique).  P is rebuilt from the saved
+// per-row log-sum-exp: P_ij = exp(scale q_i.k_j - LSE_i).
+//
+// Gradients of sum(O * dO) (plain calculus of O = softmax(scale Q K^T) V):
+//   dV = P^T dO,  dP = dO V^T,  Delta_i = sum_j P_ij dP_ij = dO_i . O_i,
+//   dS = P * (dP - Delta),  dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Three kernels, no atomics (bit-for-bit repeatable):
+//   1. delta: Delta_i = dO_i . O_i, float32, into the caller's workspace.
+//   2. dkdv:  a workgroup keeps 128 key rows resident (each wave 32 keys, K and
+//             V as VGPR operands, dK^T and dV^T accumulators in VGPRs) and
+//             streams query tiles (Q, dO row-major and transposed, LSE, Delta)
+//             through double-buffered LDS.  Per 32x32 block: S = Q K^T and
+//             dP = dO V^T leave one key per lane, so P and dS feed straight in
+//             as B operands of dV^T += dO^T P and dK^T += Q^T dS.
+//   3. dq:    a workgroup keeps 128 query rows resident (Q, dO as operands,
+//             LSE and Delta one scalar per lane) and streams key tiles (K, V
+//             row-major, K transposed).  S^T = K Q^T and dP^T = V dO^T leave
+//             one query per lane, so dS^T feeds dQ^T += K^T dS^T directly.
+// The dq kernel recomputes S and dP a second time; that costs two extra
+// contractions per tile but removes every cross-workgroup reduction.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+// ------------------------------------------------------------------ delta
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+bwd_delta_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
+                 float* __restrict__ delta, size_t rows) {
+  constexpr int TPR = D / 8;  // threads per row, 16 bytes each
+  constexpr int RPB = 256 / TPR;
+  const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 o = ld_global16(O + row * D + part * 8);
+    const u32x4 g = ld_global16(dO + row * D + part * 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = fmaf(T::to_float(elem16(o, j)), T::to_float(elem16(g, j)), acc);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && part == 0) delta[row] = acc;
+}
+
+// ------------------------------------------------------------------ dK, dV
+
+template <int D>
+struct DkvTile;
+template <>
+struct DkvTile<64> {
+  static constexpr int BR = 64;   // query rows per streamed tile
+  static constexpr int MIN_WG = 2;  // workgroups per CU the registers must allow
+};
+template <>
+struct DkvTile<128> {
+  static constexpr int BR = 32;
+  static constexpr int MIN_WG = 1;  // K, V, dK, dV of 32 rows x 128 need > 256 VGPRs
+};
+
+constexpr int kDkvKeys = 128;  // key rows per workgroup (4 waves x 32)
+
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, DkvTile<D>::MIN_WG)
+bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                const float* __restrict__ LSE, const float* __restrict__ delta,
+                uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, float c,
+                float scale, int nkt, int total) {
+  constexpr int BR = DkvTile<D>::BR;
+  constexpr int RST = D + 8;   // row-major tile stride
+  constexpr int TST = BR + 8;  // transposed tile stride
+  constexpr int RELEMS = BR * RST;
+  constexpr int TELEMS = D * TST;
+  constexpr int STAGE16 = 2 * RELEMS + 2 * TELEMS;        // Q, dO, Q^T, dO^T
+  constexpr int STAGE = STAGE16 + 2 * BR * 2;              // + LSE2, Delta (fp32)
+  constexpr int CPR = D / 8;
+  constexpr int UNITS = BR * D / 32;  // 4-row x 8-column units per tensor
+  constexpr int NDC = D / 16;
+  constexpr int NDB = D / 32;
+  static_assert(UNITS == 128, "one unit per thread, Q on threads 0-127, dO on 128-255");
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const int logical = xcd_logical_block(blockIdx.x, total);
+  const int bh = logical / nkt;
+  const int kt = logical - bh * nkt;  // causal: small kt has the most queries, runs first
+  const int k0 = kt * kDkvKeys;
+  const int wk0 = k0 + wave * 32;
+  const int mykey = wk0 + l32;
+
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const uint16_t* Qh = Q + base;
+  const uint16_t* dOh = dO + base;
+  const float* LSEh = LSE + (size_t)bh * N;
+  const float* dlth = delta + (size_t)bh * N;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+  // B operands of S = Q K^T and dP = dO V^T: lane holds row `mykey` of K, V.
+  u32x4 kf[NDC], vf[NDC];
+#pragma unroll
+  for (int cc = 0; cc < NDC; ++cc) {
+    const bool ok = mykey < N;
+    kf[cc] = ok ? ld_global16(K + base + (size_t)mykey * D + 16 * cc + 8 * hh) : zero4;
+    vf[cc] = ok ? ld_global16(V + base + (size_t)mykey * D + 16 * cc + 8 * hh) : zero4;
+  }
+
+  const int qstart = CAUSAL ? k0 : 0;  // earlier queries see none of these keys
+  const int ntiles = qstart < N ? (N - qstart + BR - 1) / BR : 0;
+
+  // ---- staging: thread < 128 loads a 4x8 unit of Q, the rest of dO ----
+  const bool is_q = tid < 128;
+  const int unit = tid & 127;
+  const int ucc = unit % CPR, urg = unit / CPR;
+  const uint16_t* src = is_q ? Qh : dOh;
+  u32x4 ur[4];
+  float sv = 0.f;
+  auto gload = [&](int qs) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int q = qs + 4 * urg + e;
+      ur[e] = q < N ? ld_global16(src + (size_t)q * D + ucc * 8) : zero4;
+    }
+    if (tid < 2 * BR) {
+      const int q = qs + (tid % BR);
+      if (tid < BR)  // LSE in log2 units; rows past N get +inf so P = 0
+        sv = q < N ? LSEh[q] * kLog2e : INFINITY;
+      else
+        sv = q < N ? dlth[q] : 0.f;
+    }
+  };
+  const int upos = tposition(4 * urg);
+  auto lstore = [&](int stage) {
+    uint16_t* S0 = smem + stage * STAGE;
+    uint16_t* R = S0 + (is_q ? 0 : RELEMS);
+    uint16_t* Tt = S0 + 2 * RELEMS + (is_q ? 0 : TELEMS);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st_lds16(R + (4 * urg + e) * RST + ucc * 8, ur[e]);
+    store_transposed4(Tt, TST, ucc * 8, upos, ur);
+    if (tid < 2 * BR) reinterpret_cast<float*>(S0 + STAGE16)[tid] = sv;
+  };
+
+  f32x16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dkacc[db][r] = 0.f;
+      dvacc[db][r] = 0.f;
+    }
+
+  if (ntiles > 0) {
+    gload(qstart);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int qs = qstart + t * BR;
+    if (t + 1 < ntiles) gload(qs + BR);
+    const uint16_t* S0 = smem + (t & 1) * STAGE;
+    const uint16_t* Qs = S0;
+    const uint16_t* dOs = S0 + RELEMS;
+    const uint16_t* Qt = S0 + 2 * RELEMS;
+    const uint16_t* dOt = Qt + TELEMS;
+    const float* lse2s = reinterpret_cast<const float*>(S0 + STAGE16);
+    const float* dlts = lse2s + BR;
+
+#pragma unroll
+    for (int qb = 0; qb < BR / 32; ++qb) {
+      const int qb0 = qs + qb * 32;
+      if (CAUSAL && qb0 + 31 < wk0) continue;  // every query precedes every key
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int cc = 0; cc < NDC; ++cc) {
+        const u32x4 aq = ld_lds16(Qs + (qb * 32 + l32) * RST + 16 * cc + 8 * hh);
+        s = T::mfma(aq, kf[cc], s);
+        const u32x4 ag = ld_lds16(dOs + (qb * 32 + l32) * RST + 16 * cc + 8 * hh);
+        dp = T::mfma(ag, vf[cc], dp);
+      }
+      // lane: key `mykey`; register r: query qb0 + 8*(r/4) + 4*hh + r%4
+      const bool need_mask = CAUSAL && qb0 < wk0 + 31;
+      u32x4 pp[2], dsp[2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qo = qb * 32 + 8 * g + 4 * hh;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qo);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlts + qo);
+        float p[4], ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float pv = exp2f(fmaf(s[r], c, -l4[e]));
+          if (need_mask && qs + qo + e < mykey) pv = 0.f;
+          p[e] = pv;
+          ds[e] = pv * (dp[r] - d4[e]);
+        }
+        pp[g >> 1][2 * (g & 1)] = T::pack2(p[0], p[1]);
+        pp[g >> 1][2 * (g & 1) + 1] = T::pack2(p[2], p[3]);
+        dsp[g >> 1][2 * (g & 1)] = T::pack2(ds[0], ds[1]);
+        dsp[g >> 1][2 * (g & 1) + 1] = T::pack2(ds[2], ds[3]);
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int qc = 0; qc < 2; ++qc) {
+          const int off = (db * 32 + l32) * TST + qb * 32 + 16 * qc + 8 * hh;
+          dvacc[db] = T::mfma(ld_lds16(dOt + off), pp[qc], dvacc[db]);
+          dkacc[db] = T::mfma(ld_lds16(Qt + off), dsp[qc], dkacc[db]);
+        }
+    }
+    if (t + 1 < ntiles) lstore((t + 1) & 1);
+    __syncthreads();
+  }
+
+  if (mykey < N) {
+    uint16_t* dKr = dK + base + (size_t)mykey * D;
+    uint16_t* dVr = dV + base + (size_t)mykey * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * hh;
+        u32x2 wk, wv;
+        wk[0] = T::pack2(dkacc[db][4 * g] * scale, dkacc[db][4 * g + 1] * scale);
+        wk[1] = T::pack2(dkacc[db][4 * g + 2] * scale, dkacc[db][4 * g + 3] * scale);
+        wv[0] = T::pack2(dvacc[db][4 * g], dvacc[db][4 * g + 1]);
+        wv[1] = T::pack2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
+        st_global8(dKr + d, wk);
+        st_global8(dVr + d, wv);
+      }
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+
+template <int D>
+struct DqTile;
+template <>
+struct DqTile<64> {
+  static constexpr int BC = 64;  // key rows per streamed tile
+};
+template <>
+struct DqTile<128> {
+  static constexpr int BC = 32;
+};
+
+constexpr int kDqBR = 128;  // query rows per workgroup (4 waves x 32)
+
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 2)
+bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+              const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+              const float* __restrict__ LSE, const float* __restrict__ delta,
+              uint16_t* __restrict__ dQ, int N, float c, float scale, int nqt, int total) {
+  constexpr int BC = DqTile<D>::BC;
+  constexpr int RST = D + 8;
+  constexpr int TST = BC + 8;
+  constexpr int RELEMS = BC * RST;
+  constexpr int STAGE = 2 * RELEMS + D * TST;  // K, V row-major; K^T
+  constexpr int CPR = D / 8;
+  constexpr int UNITS = BC * D / 32;
+  constexpr int NKB = BC / 32;
+  constexpr int NDC = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int NKC = BC / 16;
+  static_assert(UNITS == 128, "one unit per thread, K on threads 0-127, V on 128-255");
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const int logical = xcd_logical_block(blockIdx.x, total);
+  const int bh = logical / nqt;
+  int qt = logical - bh * nqt;
+  if (CAUSAL) qt = nqt - 1 - qt;
+  const int q0 = qt * kDqBR;
+  const int wq0 = q0 + wave * 32;
+  const int myq = wq0 + l32;
+
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const uint16_t* Kh = K + base;
+  const uint16_t* Vh = V + base;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+  u32x4 qf[NDC], gf[NDC];
+#pragma unroll
+  for (int cc = 0; cc < NDC; ++cc) {
+    const bool ok = myq < N;
+    qf[cc] = ok ? ld_global16(Q + base + (size_t)myq * D + 16 * cc + 8 * hh) : zero4;
+    gf[cc] = ok ? ld_global16(dO + base + (size_t)myq * D + 16 * cc + 8 * hh) : zero4;
+  }
+  const float lse2 = myq < N ? LSE[(size_t)bh * N + myq] * kLog2e : 0.f;
+  const float dlt = myq < N ? delta[(size_t)bh * N + myq] : 0.f;
+
+  const int kend = CAUSAL ? min(N, q0 + kDqBR) : N;
+  const int ntiles = (kend + BC - 1) / BC;
+
+  const bool is_k = tid < 128;
+  const int unit = tid & 127;
+  const int ucc = unit % CPR, urg = unit / CPR;
+  const uint16_t* src = is_k ? Kh : Vh;
+  u32x4 ur[4];
+  auto gload = [&](int ts) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = ts + 4 * urg + e;
+      ur[e] = key < N ? ld_global16(src + (size_t)key * D + ucc * 8) : zero4;
+    }
+  };
+  const int upos = tposition(4 * urg);
+  auto lstore = [&](int stage) {
+    uint16_t* S0 = smem + stage * STAGE;
+    uint16_t* R = S0 + (is_k ? 0 : RELEMS);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st_lds16(R + (4 * urg + e) * RST + ucc * 8, ur[e]);
+    if (is_k) store_transposed4(S0 + 2 * RELEMS, TST, ucc * 8, upos, ur);
+  };
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int ts = t * BC;
+    if (t + 1 < ntiles) gload(ts + BC);
+    const uint16_t* Ks = smem + (t & 1) * STAGE;
+    const uint16_t* Vs = Ks + RELEMS;
+    const uint16_t* Kt = Ks + 2 * RELEMS;
+
+    if (!CAUSAL || ts <= wq0 + 31) {
+      const bool need_mask = (ts + BC > N) || (CAUSAL && ts + BC - 1 > wq0);
+      u32x4 dsk[NKC];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        f32x16 s, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[r] = 0.f;
+          dp[r] = 0.f;
+        }
+#pragma unroll
+        for (int cc = 0; cc < NDC; ++cc) {
+          const int off = (kb * 32 + l32) * RST + 16 * cc + 8 * hh;
+          s = T::mfma(ld_lds16(Ks + off), qf[cc], s);
+          dp = T::mfma(ld_lds16(Vs + off), gf[cc], dp);
+        }
+        // lane: query `myq`; register r: key ts + kb*32 + 8*(r/4) + 4*hh + r%4
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float ds2[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int r = 8 * half + 2 * i + e;
+              float pv = exp2f(fmaf(s[r], c, -lse2));
+              if (need_mask) {
+                const int key = ts + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                if (key >= N || (CAUSAL && key > myq)) pv = 0.f;
+              }
+              ds2[e] = pv * (dp[r] - dlt);
+            }
+            dsk[2 * kb + half][i] = T::pack2(ds2[0], ds2[1]);
+          }
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          const u32x4 a = ld_lds16(Kt + (db * 32 + l32) * TST + 16 * kc + 8 * hh);
+          acc[db] = T::mfma(a, dsk[kc], acc[db]);
+        }
+    }
+    if (t + 1 < ntiles) lstore((t + 1) & 1);
+    __syncthreads();
+  }
+
+  if (myq < N) {
+    uint16_t* dQr = dQ + base + (size_t)myq * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = T::pack2(acc[db][4 * g] * scale, acc[db][4 * g + 1] * scale);
+        w[1] = T::pack2(acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale);
+        st_global8(dQr + db * 32 + 8 * g + 4 * hh, w);
+      }
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+
+template <typename T>
+static hipError_t delta16(const BwdArgs& a) {
+  const size_t rows = (size_t)a.B * a.H * a.N;
+  const int rpb = 256 / (a.D / 8);
+  const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
+  if (a.D == 64)
+    hipLaunchKernelGGL((bwd_delta_kernel<T, 64>), dim3(grid), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.O, (const uint16_t*)a.dO, a.delta, rows);
+  else
+    hipLaunchKernelGGL((bwd_delta_kernel<T, 128>), dim3(grid), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.O, (const uint16_t*)a.dO, a.delta, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_delta(const BwdArgs& a) {
+  return a.dtype == kBF16 ? delta16<BF16>(a) : delta16<F16>(a);
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t dkdv(const BwdArgs& a) {
+  const int nkt = (a.N + kDkvKeys - 1) / kDkvKeys;
+  const int total = nkt * a.B * a.H;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
+                     (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
+                     (const uint16_t*)a.dO, a.LSE, a.delta, (uint16_t*)a.dK, (uint16_t*)a.dV,
+                     a.N, a.scale * kLog2e, a.scale, nkt, total);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t dkdv16(const BwdArgs& a) {
+  if (a.D == 64) return a.causal ? dkdv<T, 64, true>(a) : dkdv<T, 64, false>(a);
+  return a.causal ? dkdv<T, 128, true>(a) : dkdv<T, 128, false>(a);
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a) {
+  return a.dtype == kBF16 ? dkdv16<BF16>(a) : dkdv16<F16>(a);
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t dq(const BwdArgs& a) {
+  const int nqt = (a.N + kDqBR - 1) / kDqBR;
+  const int total = nqt * a.B * a.H;
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
+                     (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
+                     (const uint16_t*)a.dO, a.LSE, a.delta, (uint16_t*)a.dQ, a.N,
+                     a.scale * kLog2e, a.scale, nqt, total);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t dq16(const BwdArgs& a) {
+  if (a.D == 64) return a.causal ? dq<T, 64, true>(a) : dq<T, 64, false>(a);
+  return a.causal ? dq<T, 128, true>(a) : dq<T, 128, false>(a);
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a) {
+  return a.dtype == kBF16 ? dq16<BF16>(a) : dq16<F16>(a);
+}
+
+}  // namespace fa

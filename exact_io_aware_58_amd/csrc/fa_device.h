@@ -1,0 +1,129 @@
+// fa_device.h -- device-side building blocks shared by the forward and
+// backward kernels: vector types, the gfx950 MFMA wrappers, 16-bit packing
+// with round-to-nearest-even, wave64 lane exchange and the XCD-aware
+// workgroup order.
+//
+// MFMA operand layout used throughout (v_mfma_f32_32x32x16_{bf16,f16},
+// D[32x32] += A[32x16] B[16x32], one wave64):
+//   A: lane l holds 8 consecutive K-slots of row m = l % 32, slot group l / 32
+//   B: lane l holds 8 consecutive K-slots of column n = l % 32, same grouping
+//   D: lane l, register r holds D[8*(r/4) + 4*(l/32) + r%4][l % 32]
+// A and B pair K-slots identically, so a contraction is correct for any
+// assignment of the reduction index to (l/32, slot) as long as both operands
+// use the same one; the kernels rely on that to feed an accumulator straight
+// back in as the next product's operand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---- element traits: 16-bit storage types with an fp32-accumulating MFMA ----
+struct BF16 {
+  using vec8 = bf16x8;
+  __device__ static inline f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // two floats -> packed pair, round to nearest even (v_cvt_pk_bf16_f32)
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static inline float to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+};
+
+struct F16 {
+  using vec8 = f16x8;
+  __device__ static inline f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    f16x2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static inline float to_float(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+  }
+};
+
+// ---- lane exchange ----
+// value held by lane l ^ 32 (the other half of the wave)
+__device__ inline float swap_halves(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+// ---- memory helpers ----
+__device__ inline u32x4 ld_global16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ inline void st_global8(void* p, u32x2 v) {
+  *reinterpret_cast<u32x2*>(p) = v;
+}
+__device__ inline u32x4 ld_lds16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ inline void st_lds16(uint16_t* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+__device__ inline void st_lds8(uint16_t* p, u32x2 v) {
+  *reinterpret_cast<u32x2*>(p) = v;
+}
+
+// Select the 16-bit element j (0..7) of a 16-byte vector.
+__device__ inline uint32_t elem16(u32x4 v, int j) {
+  uint32_t w = v[j >> 1];
+  return (j & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// ---- transposed tile staging ----
+// Position of key (or query) row `row` (a multiple of 4) inside a transposed
+// LDS tile.  Inside every 16-row chunk the four 4-row groups {0,1,2,3} are
+// stored at group positions {0,2,1,3}: the 8 consecutive positions a lane
+// reads for one 32x32x16 MFMA step (8*(l/32) .. +7 of the chunk) are then the
+// rows whose values sit in 8 consecutive accumulator registers of that lane
+// (rows 8*(r/4) + 4*(l/32) + r%4 of the 32x32 output layout).
+__device__ inline int tposition(int row) {
+  const int g = (row & 15) >> 2;
+  return (row & ~15) + (((g & 1) << 1) | (g >> 1)) * 4;
+}
+
+// Write a 4-row x 8-column block (r[e] = row e, columns col0 .. col0+7) into a
+// transposed tile T[col][position] with row stride `stride` elements.
+__device__ inline void store_transposed4(uint16_t* T, int stride, int col0, int pos,
+                                         const u32x4 (&r)[4]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    u32x2 w;
+    w[0] = elem16(r[0], j) | (elem16(r[1], j) << 16);
+    w[1] = elem16(r[2], j) | (elem16(r[3], j) << 16);
+    *reinterpret_cast<u32x2*>(T + (col0 + j) * stride + pos) = w;
+  }
+}
+
+// ---- workgroup order ----
+// Workgroups are dealt round-robin to the 8 XCDs (blockIdx.x % 8).  Remap so
+// that each XCD receives one contiguous range of logical tiles: tiles of the
+// same (batch, head) then share that XCD's L2 while they stream the same K/V.
+__device__ inline int xcd_logical_block(int pid, int total) {
+  constexpr int kXcd = 8;
+  int q = total / kXcd, r = total % kXcd;
+  int x = pid % kXcd, local = pid / kXcd;
+  return x * q + (x < r ? x : r) + local;
+}
+
+}  // namespace fa

@@ -1,0 +1,365 @@
+// fa_fwd.hip -- forward kernels: O = softmax(scale Q K^T) V and LSE.
+//
+// Pages cited (by address and title):
+//   [csdn]      adg.csdn.net/6a311d0d10ee7a33f27dee1b.html
+//               "kk的大模型论文学习笔记 第8篇: FlashAttention"
+//   [guanweilu] guanweilu.cn/article/445.html
+//               "CUDA Kernel 级别的优化：Flash Attention 为什么比 PyTorch 原生实现快 5-10 倍"
+//   [ijyty]     ijyty.com/news/1153309
+//               "Flash Attention 技术原理让 Transformer 更快更高效"
+//
+// Method ([guanweilu] "FlashAttention 的三板斧", first and second technique;
+// [csdn] "分块计算：厨房虽小，但够用" and "在线Softmax：分块了还能算对吗？"):
+// a workgroup keeps one block of query rows resident and streams the key and
+// value rows through on-chip memory one tile at a time.  Every row carries a
+// running maximum m and a running sum l; when a tile raises m the partial
+// output is scaled by exp(m_old - m_new), and the output is divided by l once
+// after the last tile.  Scores and probabilities exist only in registers.
+//
+// 16-bit kernel, gfx950 design (one workgroup = 4 waves = 128 query rows):
+//   * each wave owns 32 query rows; its Q fragments stay in VGPRs for the
+//     whole key loop (loaded once from HBM);
+//   * key/value tiles are double-buffered in LDS: K row-major, V transposed
+//     (d-major) so both MFMA operands are single 16-byte LDS reads; rows are
+//     padded by 16 bytes so the 32 rows a wave reads land in distinct banks;
+//   * the score tile is computed transposed, S^T = K Q^T, so each lane holds
+//     one query row: the row max needs one exchange between wave halves, the
+//     row sum none until the epilogue, and the O^T accumulators of a lane all
+//     belong to its row, so the rescale is a per-lane multiply;
+//   * P^T leaves the S^T accumulators already in the B-operand layout of
+//     O^T += V^T P^T; the K-slot order this implies is folded into the order
+//     in which V^T columns are stored;
+//   * exp is exp2 with scale*log2(e) folded into one FMA per score;
+//   * causal: tiles wholly above a wave's rows are skipped per wave, the
+//     workgroup stops at its last visible tile, only diagonal/tail tiles pay
+//     for the mask, and the longest query blocks are launched first.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+template <int D>
+struct FwdTile;
+template <>
+struct FwdTile<64> {
+  static constexpr int BC = 128;  // keys per tile
+};
+template <>
+struct FwdTile<128> {
+  static constexpr int BC = 64;
+};
+
+constexpr int kFwdBR = 128;  // query rows per workgroup (4 waves x 32)
+
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 2)
+fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+             const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+             float* __restrict__ LSE, int N, float c, int nqt, int total) {
+  constexpr int BC = FwdTile<D>::BC;
+  constexpr int KST = D + 8;   // LDS row stride of the K tile (elements)
+  constexpr int VST = BC + 8;  // LDS row stride of the V^T tile
+  constexpr int KELEMS = BC * KST;
+  constexpr int STAGE = KELEMS + D * VST;
+  constexpr int CPR = D / 8;            // 16-byte chunks per global row
+  constexpr int KCH = BC * CPR / 256;   // K chunks loaded per thread
+  constexpr int NKB = BC / 32;          // 32-key blocks per tile
+  constexpr int NDC = D / 16;           // reduction steps of S^T = K Q^T
+  constexpr int NDB = D / 32;           // 32-row blocks of O^T
+  constexpr int NKC = BC / 16;          // reduction steps of O^T += V^T P^T
+  static_assert(BC * D / 32 == 256, "one 4-key x 8-column V unit per thread");
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const int logical = xcd_logical_block(blockIdx.x, total);
+  const int bh = logical / nqt;
+  int qt = logical - bh * nqt;
+  if (CAUSAL) qt = nqt - 1 - qt;  // longest rows first
+  const int q0 = qt * kFwdBR;
+  const int wq0 = q0 + wave * 32;
+  const int myq = wq0 + l32;
+
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const uint16_t* Qh = Q + base;
+  const uint16_t* Kh = K + base;
+  const uint16_t* Vh = V + base;
+
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+  // B operand of S^T = K Q^T: lane (l32, hh) holds Q[myq][16c + 8hh .. +7].
+  u32x4 qf[NDC];
+#pragma unroll
+  for (int cc = 0; cc < NDC; ++cc)
+    qf[cc] = myq < N ? ld_global16(Qh + (size_t)myq * D + 16 * cc + 8 * hh) : zero4;
+
+  const int kend = CAUSAL ? min(N, q0 + kFwdBR) : N;
+  const int ntiles = (kend + BC - 1) / BC;
+
+  // ---- tile staging: global -> registers -> LDS ----
+  u32x4 kr[KCH], vr[4];
+  const int vcc = tid % CPR;  // this thread's V column chunk
+  const int vkg = tid / CPR;  // this thread's V 4-key group
+  auto gload = [&](int ts) {
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      const int id = j * 256 + tid;
+      const int row = id / CPR, cc = id % CPR;
+      const int key = ts + row;
+      kr[j] = key < N ? ld_global16(Kh + (size_t)key * D + cc * 8) : zero4;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = ts + 4 * vkg + e;
+      vr[e] = key < N ? ld_global16(Vh + (size_t)key * D + vcc * 8) : zero4;
+    }
+  };
+  // V^T columns are stored in tposition() order, so the 8 consecutive
+  // columns a lane reads for one PV step are exactly the keys whose
+  // probabilities sit in its 8 consecutive S^T accumulator registers.
+  const int vpos = tposition(4 * vkg);
+  auto lstore = [&](int stage) {
+    uint16_t* Ks = smem + stage * STAGE;
+    uint16_t* Vt = Ks + KELEMS;
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      const int id = j * 256 + tid;
+      const int row = id / CPR, cc = id % CPR;
+      st_lds16(Ks + row * KST + cc * 8, kr[j]);
+    }
+    store_transposed4(Vt, VST, vcc * 8, vpos, vr);
+  };
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m = -INFINITY;  // running max of scale*log2(e)*s over this row
+  float lpart = 0.f;    // running sum over the keys this lane holds
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int ts = t * BC;
+    if (t + 1 < ntiles) gload(ts + BC);
+    const uint16_t* Ks = smem + (t & 1) * STAGE;
+    const uint16_t* Vt = Ks + KELEMS;
+
+    if (!CAUSAL || ts <= wq0 + 31) {
+      // S^T[key][q] for the wave's 32 queries and the tile's BC keys.
+      f32x16 s[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < NDC; ++cc) {
+          const u32x4 a = ld_lds16(Ks + (kb * 32 + l32) * KST + 16 * cc + 8 * hh);
+          s[kb] = T::mfma(a, qf[cc], s[kb]);
+        }
+      }
+      const bool need_mask = (ts + BC > N) || (CAUSAL && ts + BC - 1 > wq0);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = ts + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key >= N || (CAUSAL && key > myq)) s[kb][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float mnew = fmaxf(m, mx * c);
+      const float alpha = exp2f(m - mnew);
+      m = mnew;
+
+      // P^T as the B operand of O^T += V^T P^T (registers 8*half .. +7 of
+      // block kb are the 8 K-slots of reduction step 2*kb + half).
+      u32x4 pk[NKC];
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p0 = exp2f(fmaf(s[kb][8 * half + 2 * i], c, -mnew));
+            const float p1 = exp2f(fmaf(s[kb][8 * half + 2 * i + 1], c, -mnew));
+            rs += p0 + p1;
+            pk[2 * kb + half][i] = T::pack2(p0, p1);
+          }
+      lpart = lpart * alpha + rs;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          const u32x4 a = ld_lds16(Vt + (db * 32 + l32) * VST + 16 * kc + 8 * hh);
+          oacc[db] = T::mfma(a, pk[kc], oacc[db]);
+        }
+    }
+    if (t + 1 < ntiles) lstore((t + 1) & 1);
+    __syncthreads();
+  }
+
+  // Epilogue: one division by the full row sum, then bf16/f16 (RNE) stores.
+  const float ltot = lpart + swap_halves(lpart);
+  const float inv = 1.f / ltot;
+  if (myq < N) {
+    uint16_t* Oq = O + base + (size_t)myq * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = T::pack2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+        w[1] = T::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+        st_global8(Oq + db * 32 + 8 * g + 4 * hh, w);
+      }
+    if (hh == 0) LSE[(size_t)bh * N + myq] = (m + log2f(ltot)) * kLn2;
+  }
+}
+
+// fp32 kernel: true fp32 products on the vector ALUs (no reduced-precision
+// matrix path), same online softmax.  Four lanes share one query row, each
+// holding D/4 of its q and o; a workgroup covers 64 rows and streams 32-key
+// tiles of K and V through LDS.
+constexpr int kF32BR = 64;
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256)
+fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+             const float* __restrict__ V, float* __restrict__ O,
+             float* __restrict__ LSE, int N, float c, int nqt, int total) {
+  constexpr int BK = 32;
+  constexpr int DP = D / 4;
+  __shared__ __attribute__((aligned(16))) float Ks[BK * D];
+  __shared__ __attribute__((aligned(16))) float Vs[BK * D];
+
+  const int tid = threadIdx.x;
+  const int qi = tid >> 2, part = tid & 3;
+  const int logical = xcd_logical_block(blockIdx.x, total);
+  const int bh = logical / nqt;
+  int qt = logical - bh * nqt;
+  if (CAUSAL) qt = nqt - 1 - qt;
+  const int q0 = qt * kF32BR;
+  const int myq = q0 + qi;
+  const size_t base = (size_t)bh * (size_t)N * D;
+
+  float q[DP], o[DP];
+#pragma unroll
+  for (int e = 0; e < DP; ++e) {
+    q[e] = myq < N ? Q[base + (size_t)myq * D + part * DP + e] : 0.f;
+    o[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int kend = CAUSAL ? min(N, q0 + kF32BR) : N;
+
+  for (int ts = 0; ts < kend; ts += BK) {
+    __syncthreads();
+    for (int i = tid; i < BK * D / 4; i += 256) {
+      const int row = (i * 4) / D, col = (i * 4) % D;
+      const int key = ts + row;
+      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      if (key < N) {
+        kv = *reinterpret_cast<const f32x4*>(K + base + (size_t)key * D + col);
+        vv = *reinterpret_cast<const f32x4*>(V + base + (size_t)key * D + col);
+      }
+      *reinterpret_cast<f32x4*>(Ks + row * D + col) = kv;
+      *reinterpret_cast<f32x4*>(Vs + row * D + col) = vv;
+    }
+    __syncthreads();
+
+    float s[BK];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < BK; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < DP; ++e) acc = fmaf(q[e], Ks[j * D + part * DP + e], acc);
+      acc += __shfl_xor(acc, 1, 64);
+      acc += __shfl_xor(acc, 2, 64);
+      const int key = ts + j;
+      if (key >= N || (CAUSAL && key > myq)) acc = -INFINITY;
+      s[j] = acc;
+      mx = fmaxf(mx, acc);
+    }
+    const float mnew = fmaxf(m, mx * c);
+    const float alpha = exp2f(m - mnew);
+    m = mnew;
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < DP; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int j = 0; j < BK; ++j) {
+      const float p = exp2f(fmaf(s[j], c, -mnew));
+      l += p;
+#pragma unroll
+      for (int e = 0; e < DP; ++e) o[e] = fmaf(p, Vs[j * D + part * DP + e], o[e]);
+    }
+  }
+  if (myq < N) {
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int e = 0; e < DP; ++e) O[base + (size_t)myq * D + part * DP + e] = o[e] * inv;
+    if (part == 0) LSE[(size_t)bh * N + myq] = (m + log2f(l)) * kLn2;
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t launch16(const FwdArgs& a) {
+  const int nqt = (a.N + kFwdBR - 1) / kFwdBR;
+  const int total = nqt * a.B * a.H;
+  hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
+                     (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
+                     (uint16_t*)a.O, a.LSE, a.N, a.scale * kLog2e, nqt, total);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch32(const FwdArgs& a) {
+  const int nqt = (a.N + kF32BR - 1) / kF32BR;
+  const int total = nqt * a.B * a.H;
+  hipLaunchKernelGGL((fwd32_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
+                     (const float*)a.Q, (const float*)a.K, (const float*)a.V, (float*)a.O,
+                     a.LSE, a.N, a.scale * kLog2e, nqt, total);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t dispatch16(const FwdArgs& a) {
+  if (a.D == 64) return a.causal ? launch16<T, 64, true>(a) : launch16<T, 64, false>(a);
+  return a.causal ? launch16<T, 128, true>(a) : launch16<T, 128, false>(a);
+}
+
+hipError_t launch_fwd(const FwdArgs& a) {
+  switch (a.dtype) {
+    case kF32:
+      if (a.D == 64) return a.causal ? launch32<64, true>(a) : launch32<64, false>(a);
+      return a.causal ? launch32<128, true>(a) : launch32<128, false>(a);
+    case kBF16:
+      return dispatch16<BF16>(a);
+    default:
+      return dispatch16<F16>(a);
+  }
+}
+
+}  // namespace fa

@@ -1,0 +1,48 @@
+// fa_launch.h -- host-side interface between the C ABI (fa_api.hip) and the
+// kernel launchers.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+enum Dtype { kF32 = 0, kBF16 = 1, kF16 = 2 };
+
+struct FwdArgs {
+  int dtype, B, H, N, D;
+  float scale;
+  int causal;
+  const void *Q, *K, *V;
+  void* O;
+  float* LSE;
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  int dtype, B, H, N, D;
+  float scale;
+  int causal;
+  const void *Q, *K, *V, *O, *dO;
+  const float* LSE;
+  void *dQ, *dK, *dV;
+  float* delta;  // [B, H, N] float32 scratch inside the caller's workspace
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd(const FwdArgs& a);
+// Each backward launcher enqueues one kernel.
+hipError_t launch_bwd_delta(const BwdArgs& a);
+hipError_t launch_bwd_dkdv(const BwdArgs& a);
+hipError_t launch_bwd_dq(const BwdArgs& a);
+
+// Optional per-kernel event timing (fa_timing.cpp).  No-ops when disabled.
+struct TimedLaunch {
+  TimedLaunch(int kernel_id, hipStream_t s);
+  ~TimedLaunch();
+  int id;
+  hipStream_t stream;
+  int slot;
+};
+
+}  // namespace fa

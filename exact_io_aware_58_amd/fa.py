@@ -1,0 +1,165 @@
+"""ctypes binding of libfa.so (C ABI in include/fa.h).
+
+Argument marshalling only: every step of attention runs in the library's HIP
+kernels.  The raw entry points keep the C names and take integers (device
+addresses, stream handles); ``forward``/``backward`` are conveniences that
+allocate outputs with torch (device memory and streams are the only things
+torch is used for) and pass ``tensor.data_ptr()`` and the current stream.
+
+Loading fails loudly if the library has not been built: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_F32, FA_BF16, FA_F16 = 0, 1, 2
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
+FA_KERNEL_FWD, FA_KERNEL_BWD_DELTA, FA_KERNEL_BWD_DKDV, FA_KERNEL_BWD_DQ = 0, 1, 2, 3
+FA_KERNEL_COUNT = 4
+
+# Every symbol include/fa.h declares, with (restype, argtypes).
+_c_int, _c_size, _vp, _f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+SIGNATURES = {
+    "fa_fwd": (_c_int, [_c_int] * 5 + [_f, _c_int] + [_vp] * 6),
+    "fa_bwd_workspace_bytes": (_c_size, [_c_int] * 6),
+    "fa_bwd": (_c_int, [_c_int] * 5 + [_f, _c_int] + [_vp] * 10 + [_c_size, _vp]),
+    "fa_status_string": (ctypes.c_char_p, [_c_int]),
+    "fa_version": (_c_int, []),
+    "fa_timing_enable": (_c_int, [_c_int]),
+    "fa_timing_read": (_c_int, [_c_int, ctypes.POINTER(ctypes.c_longlong),
+                                ctypes.POINTER(ctypes.c_double),
+                                ctypes.POINTER(ctypes.c_longlong)]),
+    "fa_kernel_name": (ctypes.c_char_p, [_c_int]),
+}
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_string(status)} ({status})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(the HIP library is the only compute path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+# ---------------------------------------------------------------- raw C ABI
+
+def fa_fwd(dtype, B, H, N, D, scale, causal, Q, K, V, O, LSE, stream) -> int:
+    return _lib.fa_fwd(dtype, B, H, N, D, scale, int(causal), Q, K, V, O, LSE, stream)
+
+
+def fa_bwd_workspace_bytes(dtype, B, H, N, D, causal) -> int:
+    return _lib.fa_bwd_workspace_bytes(dtype, B, H, N, D, int(causal))
+
+
+def fa_bwd(dtype, B, H, N, D, scale, causal, Q, K, V, O, dO, LSE, dQ, dK, dV,
+           workspace, workspace_bytes, stream) -> int:
+    return _lib.fa_bwd(dtype, B, H, N, D, scale, int(causal), Q, K, V, O, dO, LSE,
+                       dQ, dK, dV, workspace, workspace_bytes, stream)
+
+
+def fa_status_string(status: int) -> str:
+    return _lib.fa_status_string(status).decode()
+
+
+def fa_version() -> int:
+    return _lib.fa_version()
+
+
+def fa_timing_enable(on: bool) -> int:
+    return _lib.fa_timing_enable(1 if on else 0)
+
+
+def fa_timing_read(kernel_id: int):
+    """(launches, total_ms, dropped) for one kernel id."""
+    n, ms, dr = ctypes.c_longlong(), ctypes.c_double(), ctypes.c_longlong()
+    rc = _lib.fa_timing_read(kernel_id, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(dr))
+    if rc != FA_OK:
+        raise FAError(rc, "fa_timing_read")
+    return n.value, ms.value, dr.value
+
+
+def fa_kernel_name(kernel_id: int) -> str:
+    return _lib.fa_kernel_name(kernel_id).decode()
+
+
+# ---------------------------------------------------------------- torch helpers
+
+def _dtype_code(t):
+    import torch
+    codes = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.float16: FA_F16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _check_qkv(*ts):
+    shape, dtype = ts[0].shape, ts[0].dtype
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
+        if t.shape != shape or t.dtype != dtype:
+            raise ValueError("tensors must share one (B, H, N, D) shape and dtype")
+    if len(shape) != 4:
+        raise ValueError("expected (B, H, N, D) tensors")
+    return shape
+
+
+def _stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def forward(q, k, v, scale, causal=False, out=None, lse=None):
+    """(O, LSE) for (B, H, N, D) tensors; LSE is float32 (B, H, N)."""
+    import torch
+    B, H, N, D = _check_qkv(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    rc = fa_fwd(_dtype_code(q), B, H, N, D, float(scale), causal, q.data_ptr(), k.data_ptr(),
+                v.data_ptr(), out.data_ptr(), lse.data_ptr(), _stream())
+    if rc != FA_OK:
+        raise FAError(rc, "fa_fwd")
+    return out, lse
+
+
+def workspace_bytes(q, causal=False):
+    B, H, N, D = q.shape
+    return fa_bwd_workspace_bytes(_dtype_code(q), B, H, N, D, causal)
+
+
+def backward(q, k, v, o, do, lse, scale, causal=False, dq=None, dk=None, dv=None,
+             workspace=None):
+    """(dQ, dK, dV) of sum(O * dO), recomputing P from LSE."""
+    import torch
+    B, H, N, D = _check_qkv(q, k, v, o, do)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    need = workspace_bytes(q, causal)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    rc = fa_bwd(_dtype_code(q), B, H, N, D, float(scale), causal, q.data_ptr(), k.data_ptr(),
+                v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                _stream())
+    if rc != FA_OK:
+        raise FAError(rc, "fa_bwd")
+    return dq, dk, dv

@@ -1,0 +1,137 @@
+/*
+ * fa.h -- C ABI of libfa.so: FlashAttention fused exact attention on AMD
+ * MI355X (gfx950), forward and backward.
+ *
+ * Pages cited (by address and title):
+ *   [csdn]      adg.csdn.net/6a311d0d10ee7a33f27dee1b.html
+ *               "kk的大模型论文学习笔记 第8篇: FlashAttention"
+ *   [guanweilu] guanweilu.cn/article/445.html
+ *               "CUDA Kernel 级别的优化：Flash Attention 为什么比 PyTorch 原生实现快 5-10 倍"
+ *   [ijyty]     ijyty.com/news/1153309
+ *               "Flash Attention 技术原理让 Transformer 更快更高效"
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are (batch B, heads H, sequence N, head dim D), contiguous,
+ *     row stride D elements ([ijyty] "传统 Attention 的问题": the
+ *     (batch, heads, seq_len, head_dim) layout).  Self-attention: queries and
+ *     keys share N.
+ *   - All tensor pointers are DEVICE pointers owned by the caller and must be
+ *     16-byte aligned.  The library never allocates, frees or synchronises;
+ *     it only enqueues kernels on `stream` (a hipStream_t; NULL = the null
+ *     stream) and returns.  Device faults surface at the caller's next
+ *     synchronisation.
+ *   - Arguments are validated before any HIP call; on an error nothing is
+ *     launched and no output is touched.
+ *   - causal != 0 keeps key j for query i iff j <= i (diagonal included).
+ *     The pages do not define the mask; this is the usual autoregressive one.
+ *   - scale multiplies Q K^T before the softmax; it must be finite and > 0
+ *     (the pages use 1/sqrt(D): [ijyty] naive_attention snippet).
+ *   - Entry points are stateless and may be called from several host threads
+ *     (the optional kernel timer below is guarded by a mutex).
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V, O, dO, dQ, dK, dV. */
+typedef enum {
+  FA_F32 = 0,   /* float32: checked at 1e-5 against the float64 oracle     */
+  FA_BF16 = 1,  /* bfloat16 storage, fp32 accumulation, bf16 MFMA          */
+  FA_F16 = 2    /* IEEE half storage, fp32 accumulation, f16 MFMA          */
+} fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, B/H/N <= 0, size overflow, bad scale */
+  FA_ERR_UNSUPPORTED = -2,  /* D not in {64, 128} or unknown dtype                         */
+  FA_ERR_WORKSPACE = -3,    /* backward workspace missing or smaller than required          */
+  FA_ERR_HIP = -4           /* a kernel launch failed (hipGetLastError after the launch)    */
+} fa_status;
+
+/*
+ * fa_fwd -- O = softmax(scale * Q K^T) V, computed tile by tile with the
+ * online softmax (per-row running max m and running sum l; the partial output
+ * is rescaled whenever m grows and divided by l once at the end):
+ * [guanweilu] "FlashAttention 的三板斧", first technique (tiling: S and P
+ * live only on chip) and second technique (online softmax); [csdn]
+ * "在线Softmax：分块了还能算对吗？".  The N x N score matrix never reaches HBM.
+ *
+ *   Q, K, V : [B, H, N, D] of `dtype`, read only.
+ *   O       : [B, H, N, D] of `dtype`, written (bf16/f16: round to nearest even).
+ *   LSE     : [B, H, N] float32, written: LSE_i = m_i + ln(l_i), the natural
+ *             log of row i's softmax normaliser of the scaled, masked scores.
+ *             The backward pass reads it to recompute P.
+ *   D       : 64 or 128.  Any N >= 1 (ragged tails are masked).
+ * Returns an fa_status.
+ */
+int fa_fwd(int dtype, int B, int H, int N, int D, float scale, int causal,
+           const void* Q, const void* K, const void* V, void* O, float* LSE,
+           void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for this problem (the per-row
+ * Delta_i = dO_i . O_i, float32 [B, H, N], padded to 256 bytes).  Returns 0
+ * for invalid sizes.
+ */
+size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int D, int causal);
+
+/*
+ * fa_bwd -- gradients of sum(O * dO) with respect to Q, K and V.  S and P are
+ * recomputed on chip from Q, K and the saved LSE instead of being stored
+ * ([csdn] "重计算：扔掉比存着更快"; [guanweilu] "FlashAttention 的三板斧",
+ * third technique).  With P_ij = exp(scale q_i.k_j - LSE_i):
+ *   dV = P^T dO,  dP = dO V^T,  Delta_i = dO_i . O_i,
+ *   dS = P * (dP - Delta),  dQ = scale dS K,  dK = scale dS^T Q.
+ * Three kernels on `stream`: Delta, then dK/dV (key tiles resident, query
+ * tiles streamed), then dQ (query tiles resident, key tiles streamed).  No
+ * atomics: the result is bit-for-bit repeatable.
+ *
+ *   Q, K, V, O, dO : [B, H, N, D] of `dtype`, read only (O and LSE from fa_fwd
+ *                    with the same arguments).
+ *   LSE            : [B, H, N] float32 from fa_fwd, read only.
+ *   dQ, dK, dV     : [B, H, N, D] of `dtype`, written.
+ *   workspace      : device buffer of at least fa_bwd_workspace_bytes(...)
+ *                    bytes, 16-byte aligned, owned by the caller; contents on
+ *                    entry are ignored.  FA_ERR_WORKSPACE if too small.
+ */
+int fa_bwd(int dtype, int B, int H, int N, int D, float scale, int causal,
+           const void* Q, const void* K, const void* V, const void* O,
+           const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static English text for a status code. */
+const char* fa_status_string(int status);
+
+/* Library ABI version (increments on any signature change). */
+int fa_version(void);
+
+/*
+ * Per-kernel device timing (measurement support, off by default).  While
+ * enabled, every launch is bracketed by two hipEvents recorded on the launch
+ * stream; fa_timing_read synchronises those events and returns, for one
+ * kernel id, the number of timed launches and their summed duration in
+ * milliseconds.  fa_timing_enable(1) also clears previous totals.  Events
+ * come from a fixed pool of 8192 pairs created at enable time; launches
+ * beyond it are not timed (counted in *dropped).
+ */
+enum {
+  FA_KERNEL_FWD = 0,          /* forward kernel                          */
+  FA_KERNEL_BWD_DELTA = 1,    /* backward: Delta = rowsum(dO * O)        */
+  FA_KERNEL_BWD_DKDV = 2,     /* backward: dK, dV                        */
+  FA_KERNEL_BWD_DQ = 3,       /* backward: dQ                            */
+  FA_KERNEL_COUNT = 4
+};
+int fa_timing_enable(int on);
+int fa_timing_read(int kernel_id, long long* launches, double* total_ms, long long* dropped);
+const char* fa_kernel_name(int kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,57 @@
+"""Helpers for GPU parity tests: move seeded inputs to the device, call the
+HIP library through its binding, bring results back as float64."""
+from __future__ import annotations
+
+import numpy as np
+
+from exact_io_aware_58_amd import inputs
+
+# Tolerances.  fp32: max abs 1e-5 on O and LSE.  16-bit storage: max abs
+# 2e-2 on O; dQ, dK, dV max|err| / max|ref| <= 5e-2 per tensor; LSE (fp32
+# output computed from fp32 scores) max abs 1e-3.
+TOL = {
+    "f32": dict(o=1e-5, lse=1e-5),
+    "bf16": dict(o=2e-2, lse=1e-3, grad_rel=5e-2),
+    "f16": dict(o=2e-2, lse=1e-3, grad_rel=5e-2),
+}
+
+
+def torch_dtype(name):
+    import torch
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[name]
+
+
+def to_device(raw: np.ndarray, dtype: str):
+    """Upload the raw storage array produced by exact_io_aware_58_amd.inputs."""
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(raw)).cuda()
+
+
+def to_f64(t) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def draw_case(seed, shape, dtype, mult=1.0, grad=False):
+    names = ["q", "k", "v"] + (["do"] if grad else [])
+    vals, devs = {}, {}
+    for n in names:
+        x, raw = inputs.draw(seed, n, shape, dtype, mult)
+        vals[n] = x.astype(np.float64)
+        devs[n] = to_device(raw, dtype)
+    return vals, devs
+
+
+def max_abs(a, b):
+    return float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) if np.size(a) else 0.0
+
+
+def rel_to_max(a, ref):
+    ref = np.asarray(ref)
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    return max_abs(a, ref) / den if den > 0 else max_abs(a, ref)
+
+
+def say(msg):
+    print(msg, flush=True)

@@ -1,0 +1,120 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and rejects bad arguments before making any HIP call."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+LIB = os.path.join(ROOT, "exact_io_aware_58_amd", "libfa.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libfa.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_api():
+    assert {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string"} <= set(_declared())
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [s for s in _declared() if s not in exported]
+    assert not missing, missing
+
+
+def test_binding_names_match_header():
+    from exact_io_aware_58_amd import fa
+    assert sorted(fa.SIGNATURES) == _declared()
+    for name in _declared():
+        assert callable(getattr(fa, name))
+
+
+@pytest.fixture(scope="module")
+def fa():
+    from exact_io_aware_58_amd import fa as mod
+    return mod
+
+
+A = 0x10000  # aligned fake device addresses: validation rejects before any use
+P = [A + 0x1000 * i for i in range(12)]
+
+
+def test_version_and_status_strings(fa):
+    assert fa.fa_version() >= 1
+    for code in (0, -1, -2, -3, -4):
+        assert fa.fa_status_string(code) != "unknown status"
+    assert fa.fa_status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(dtype=7), -2),
+    (dict(D=96), -2),
+    (dict(D=32), -2),
+    (dict(B=0), -1),
+    (dict(H=-1), -1),
+    (dict(N=0), -1),
+    (dict(N=1 << 25), -1),
+    (dict(scale=0.0), -1),
+    (dict(scale=-0.125), -1),
+    (dict(scale=float("inf")), -1),
+    (dict(scale=float("nan")), -1),
+])
+def test_fwd_rejects_bad_problem(fa, args, status):
+    kw = dict(dtype=fa.FA_BF16, B=1, H=2, N=128, D=64, scale=0.125)
+    kw.update(args)
+    rc = fa.fa_fwd(kw["dtype"], kw["B"], kw["H"], kw["N"], kw["D"], kw["scale"], 0,
+                   P[0], P[1], P[2], P[3], P[4], None)
+    assert rc == status
+
+
+@pytest.mark.parametrize("which", range(5))
+@pytest.mark.parametrize("bad", [0, A + 8])
+def test_fwd_rejects_null_or_misaligned(fa, which, bad):
+    ptrs = P[:5]
+    ptrs[which] = bad
+    assert fa.fa_fwd(fa.FA_BF16, 1, 2, 128, 64, 0.125, 0, *ptrs, None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_workspace_bytes(fa):
+    assert fa.fa_bwd_workspace_bytes(fa.FA_BF16, 8, 12, 1024, 64, 1) == 8 * 12 * 1024 * 4
+    assert fa.fa_bwd_workspace_bytes(fa.FA_BF16, 1, 1, 3, 64, 0) == 256  # padded
+    assert fa.fa_bwd_workspace_bytes(fa.FA_BF16, 1, 1, 3, 96, 0) == 0
+    assert fa.fa_bwd_workspace_bytes(fa.FA_F32, 1, 1, 128, 64, 0) == 0
+
+
+def _bwd(fa, dtype=None, ws_bytes=None, ws=P[10], ptr_over=None, D=64, N=128):
+    dtype = fa.FA_BF16 if dtype is None else dtype
+    ptrs = P[:9]
+    if ptr_over:
+        ptrs[ptr_over[0]] = ptr_over[1]
+    if ws_bytes is None:
+        ws_bytes = fa.fa_bwd_workspace_bytes(fa.FA_BF16, 1, 2, N, 64, 0)
+    return fa.fa_bwd(dtype, 1, 2, N, D, 0.125, 0, *ptrs, ws, ws_bytes, None)
+
+
+def test_bwd_validation(fa):
+    assert _bwd(fa, ws_bytes=16) == fa.FA_ERR_WORKSPACE
+    assert _bwd(fa, ws=0) == fa.FA_ERR_WORKSPACE
+    assert _bwd(fa, ws=A + 4) == fa.FA_ERR_INVALID_ARG
+    assert _bwd(fa, dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert _bwd(fa, D=80) == fa.FA_ERR_UNSUPPORTED
+    for i in range(9):
+        assert _bwd(fa, ptr_over=(i, 0)) == fa.FA_ERR_INVALID_ARG
+        assert _bwd(fa, ptr_over=(i, A + 2)) == fa.FA_ERR_INVALID_ARG
+
+
+def test_timing_read_bounds(fa):
+    with pytest.raises(fa.FAError):
+        fa.fa_timing_read(fa.FA_KERNEL_COUNT)
+    n, ms, dropped = fa.fa_timing_read(fa.FA_KERNEL_FWD)
+    assert n == 0 and ms == 0.0 and dropped == 0
+    assert [fa.fa_kernel_name(i) for i in range(4)] == ["fwd", "bwd_delta", "bwd_dkdv", "bwd_dq"]

@@ -1,0 +1,219 @@
+"""Parity of the HIP path (through the C ABI) with the CPU float64 oracle.
+
+Small shapes are compared element by element over every output; they span
+several tiles and ragged tails (N not a multiple of any tile size), both
+masks, both head dims and every dtype.  The five workloads run at full size
+in the same launch configuration the bench times; where the oracle cannot
+cover every row (N = 16384 and 65536) it checks seeded row subsets that
+always include tile edges and the causal diagonal.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from exact_io_aware_58_amd import inputs
+from tests.gpu_util import TOL, draw_case, max_abs, rel_to_max, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from exact_io_aware_58_amd import fa  # noqa: E402  (fails loudly if libfa.so is missing)
+
+SHAPES_N = [1, 17, 63, 64, 65, 127, 128, 129, 255, 1000]
+
+
+def _fwd(devs, scale, causal):
+    o, lse = fa.forward(devs["q"], devs["k"], devs["v"], scale, causal)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", SHAPES_N)
+def test_forward_small(N, causal, D, dtype):
+    say(f"[fwd] N={N} D={D} causal={causal} dtype={dtype}")
+    shape = (1, 2, N, D)
+    vals, devs = draw_case(100 + N, shape, dtype)
+    scale = 1.0 / np.sqrt(D)
+    o, lse = _fwd(devs, scale, causal)
+    ro, rl = oracle.attention_fwd(vals["q"], vals["k"], vals["v"], scale, causal)
+    tol = TOL[dtype]
+    assert max_abs(to_f64(o), ro) <= tol["o"]
+    assert max_abs(to_f64(lse), rl) <= tol["lse"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", SHAPES_N)
+def test_backward_small(N, causal, D, dtype):
+    say(f"[bwd] N={N} D={D} causal={causal} dtype={dtype}")
+    shape = (1, 2, N, D)
+    vals, devs = draw_case(200 + N, shape, dtype, grad=True)
+    scale = 1.0 / np.sqrt(D)
+    o, lse = _fwd(devs, scale, causal)
+    dq, dk, dv = fa.backward(devs["q"], devs["k"], devs["v"], o, devs["do"], lse, scale, causal)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_bwd(vals["q"], vals["k"], vals["v"], vals["do"], scale, causal)
+    tol = TOL[dtype]["grad_rel"]
+    eq, ek, ev = rel_to_max(to_f64(dq), rq), rel_to_max(to_f64(dk), rk), rel_to_max(to_f64(dv), rv)
+    say(f"    rel-to-max dQ={eq:.2e} dK={ek:.2e} dV={ev:.2e}")
+    assert eq <= tol and ek <= tol and ev <= tol
+
+
+def test_output_rounding_is_nearest_even():
+    """N = 2 with identical keys gives weights of exactly 1/2, so O is the
+    exact fp32 mean of two bf16 values; pick means that sit exactly halfway
+    between two bf16 numbers (ties go to the even one) and just above a
+    halfway point (must round up, where truncation would round down)."""
+    D = 64
+    q = np.zeros((1, 1, 2, D), np.float32)
+    k = np.zeros((1, 1, 2, D), np.float32)
+    v = np.zeros((1, 1, 2, D), np.float32)
+    u = 2.0 ** -7
+    pairs = [(1.0, 1.0 + 2 * u), (1.0 + u, 1.0 + 2 * u), (1.0 + u, 1.0 + 4 * u),
+             (-1.0 - u, -1.0 - 2 * u), (2.0, 2.0 + 4 * u)]
+    exp_bits = []
+    for d in range(D):
+        a, b = pairs[d % len(pairs)]
+        v[0, 0, 0, d], v[0, 0, 1, d] = a, b
+    from exact_io_aware_58_amd.inputs import round_bf16_bits
+    mean = ((v[0, 0, 0].astype(np.float64) + v[0, 0, 1]) / 2).astype(np.float32)
+    exp_bits = round_bf16_bits(mean)
+    devs = {n: torch.from_numpy(x).cuda().to(torch.bfloat16) for n, x in (("q", q), ("k", k), ("v", v))}
+    o, _ = _fwd(devs, 0.125, False)
+    got = o.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got[0, 0, 0], exp_bits)
+    assert np.array_equal(got[0, 0, 1], exp_bits)
+
+
+def test_forward_and_backward_are_repeatable():
+    """No atomics anywhere: two runs give identical bits."""
+    w = inputs.WORKLOADS["c3"]
+    vals, devs = draw_case(w.seed, (2, 4, 700, 64), "bf16", grad=True)
+    outs = []
+    for _ in range(2):
+        o, lse = _fwd(devs, 0.125, True)
+        g = fa.backward(devs["q"], devs["k"], devs["v"], o, devs["do"], lse, 0.125, True)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (o, lse, *g)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------ five workloads
+
+def _workload_devs(w):
+    return draw_case(w.seed, w.shape, w.dtype, w.input_mult, grad=w.backward)
+
+
+def test_workload_c1_fp32_forward():
+    w = inputs.WORKLOADS["c1"]
+    say(f"[{w.name}]")
+    vals, devs = _workload_devs(w)
+    o, lse = _fwd(devs, w.scale, w.causal)
+    ro, rl = oracle.attention_fwd(vals["q"], vals["k"], vals["v"], w.scale, w.causal)
+    eo, el = max_abs(to_f64(o), ro), max_abs(to_f64(lse), rl)
+    say(f"    max abs O={eo:.2e} LSE={el:.2e}")
+    assert eo <= 1e-5 and el <= 1e-5
+
+
+def test_workload_c2_bf16_forward():
+    w = inputs.WORKLOADS["c2"]
+    say(f"[{w.name}]")
+    vals, devs = _workload_devs(w)
+    o, lse = _fwd(devs, w.scale, w.causal)
+    ro, rl = oracle.attention_fwd(vals["q"], vals["k"], vals["v"], w.scale, w.causal)
+    eo, el = max_abs(to_f64(o), ro), max_abs(to_f64(lse), rl)
+    say(f"    max abs O={eo:.2e} (rel-to-max {rel_to_max(to_f64(o), ro):.2e}) LSE={el:.2e}")
+    assert eo <= 2e-2 and el <= 1e-3
+
+
+def test_workload_c3_causal_training_step():
+    w = inputs.WORKLOADS["c3"]
+    say(f"[{w.name}]")
+    vals, devs = _workload_devs(w)
+    o, lse = _fwd(devs, w.scale, True)
+    dq, dk, dv = fa.backward(devs["q"], devs["k"], devs["v"], o, devs["do"], lse, w.scale, True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_fwd(vals["q"], vals["k"], vals["v"], w.scale, True)
+    rq, rk, rv = oracle.attention_bwd(vals["q"], vals["k"], vals["v"], vals["do"], w.scale, True)
+    eo, el = max_abs(to_f64(o), ro), max_abs(to_f64(lse), rl)
+    eq, ek, ev = rel_to_max(to_f64(dq), rq), rel_to_max(to_f64(dk), rk), rel_to_max(to_f64(dv), rv)
+    say(f"    O={eo:.2e} LSE={el:.2e} dQ={eq:.2e} dK={ek:.2e} dV={ev:.2e}")
+    assert eo <= 2e-2 and el <= 1e-3
+    assert eq <= 5e-2 and ek <= 5e-2 and ev <= 5e-2
+
+
+def _sampled(t, rows):
+    idx = torch.from_numpy(rows).to(t.device)
+    return to_f64(t[idx[:, 0], idx[:, 1], idx[:, 2]])
+
+
+def test_workload_c4_long_forward_subset():
+    w = inputs.WORKLOADS["c4"]
+    say(f"[{w.name}]")
+    vals, devs = _workload_devs(w)
+    before = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    o, lse = _fwd(devs, w.scale, w.causal)
+    peak_extra = torch.cuda.max_memory_allocated() - before
+    # O(N) device memory: the outputs (O and LSE) and nothing of size N x N
+    assert peak_extra <= o.numel() * 2 + lse.numel() * 4 + (1 << 21)
+    rows = inputs.check_row_subset(w)
+    ro, rl = oracle.attention_fwd_rows(vals["q"], vals["k"], vals["v"], w.scale, w.causal, rows)
+    eo = max_abs(_sampled(o, rows), ro)
+    el = max_abs(to_f64(lse)[tuple(rows.T)], rl)
+    say(f"    {len(rows)} rows: max abs O={eo:.2e} LSE={el:.2e}")
+    assert eo <= 2e-2 and el <= 1e-3
+
+
+def _key_rows_two_heads(w, count=128):
+    """Key rows for dK/dV at N = 65536: the tile-edge rows of the first and
+    last head plus seeded rows of those two heads (each checked key row needs
+    a full pass over its head's queries in the oracle)."""
+    fixed = inputs.check_row_subset(w, count=16)[:16]
+    rng = np.random.default_rng(w.seed + 2000)
+    rows = [tuple(r) for r in fixed]
+    seen = set(rows)
+    while len(rows) < count:
+        h = (0, w.H - 1)[int(rng.integers(2))]
+        r = (0, h, int(rng.integers(w.N)))
+        if r not in seen:
+            seen.add(r)
+            rows.append(r)
+    return np.array(rows, dtype=np.int64)
+
+
+def test_workload_c5_long_causal_training_subset():
+    w = inputs.WORKLOADS["c5"]
+    say(f"[{w.name}]")
+    vals, devs = _workload_devs(w)
+    o, lse = _fwd(devs, w.scale, True)
+    dq, dk, dv = fa.backward(devs["q"], devs["k"], devs["v"], o, devs["do"], lse, w.scale, True)
+    torch.cuda.synchronize()
+    qrows = inputs.check_row_subset(w)
+    ro, rl = oracle.attention_fwd_rows(vals["q"], vals["k"], vals["v"], w.scale, True, qrows)
+    rq = oracle.attention_bwd_query_rows(vals["q"], vals["k"], vals["v"], vals["do"], w.scale,
+                                         True, qrows)
+    eo = max_abs(_sampled(o, qrows), ro)
+    el = max_abs(to_f64(lse)[tuple(qrows.T)], rl)
+    eq = rel_to_max(_sampled(dq, qrows), rq)
+    say(f"    {len(qrows)} query rows: O={eo:.2e} LSE={el:.2e} dQ={eq:.2e}")
+    krows = _key_rows_two_heads(w)
+    stats = {}
+    for h in sorted({int(r[1]) for r in krows}):
+        say(f"    oracle row statistics of head {h} ...")
+        stats[(0, h)] = oracle.row_stats(vals["q"], vals["k"], vals["v"], vals["do"], w.scale,
+                                         True, 0, h, block_rows=1024)
+    rk, rv = oracle.attention_bwd_key_rows(vals["q"], vals["k"], vals["v"], vals["do"], w.scale,
+                                           True, krows, stats=stats)
+    ek, ev = rel_to_max(_sampled(dk, krows), rk), rel_to_max(_sampled(dv, krows), rv)
+    say(f"    {len(krows)} key rows: dK={ek:.2e} dV={ev:.2e}")
+    assert eo <= 2e-2 and el <= 1e-3 and eq <= 5e-2
+    assert ek <= 5e-2 and ev <= 5e-2
