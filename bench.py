@@ -167,10 +167,13 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c5", help="c1..c5 (default c5)")
-    ap.add_argument("--cpu-rows", type=int, default=16384,
+    ap.add_argument("--cpu-rows", type=int, default=32768,
                     help="rows of the oracle sample timed for cpu_baseline (0: skip)")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the N=16384 D=128 forward-only figure")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (a "
+                         "known-size kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -214,6 +217,17 @@ def main():
         secondary = {"workload": w4.name, "pass": "fwd", "ms": ms4,
                      "tflops": f4 / (ms4 / 1e3) / 1e12,
                      "pct_of_bf16_peak": 100.0 * f4 / (ms4 / 1e3) / 1e12 / PEAK_BF16_TFLOPS}
+
+    if args.copy_mib > 0:
+        import torch
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {args.copy_mib} MiB read + {args.copy_mib} MiB written")
+        del src, dst
 
     cpu = cpu_baseline(w, args.cpu_rows) if args.cpu_rows > 0 else None
 
