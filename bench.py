@@ -60,6 +60,39 @@ def kernel_algorithmic(w):
     }
 
 
+KERNEL_SOURCES = {
+    "fwd": ["fa_fwd.hip", "fa_device.h"],
+    "bwd_delta": ["fa_bwd.hip", "fa_device.h"],
+    "bwd_dkdv": ["fa_bwd.hip", "fa_device.h"],
+    "bwd_dq": ["fa_bwd.hip", "fa_device.h"],
+}
+
+
+def source_sha(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "exact_io_aware_58_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary of this workload (FETCH_SIZE and WRITE_SIZE scaled by a plain
+    copy of known size), or None when there is none or the kernel's source
+    has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}.md")
+    if not os.path.exists(path):
+        return None
+    want = source_sha(kernel)
+    for line in open(path, encoding="utf-8"):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 7 and cells[0] == kernel and cells[6] == want:
+            return float(cells[4]) + float(cells[5])
+    return None
+
+
 def upload(raw, dtype):
     import numpy as np
     import torch
@@ -251,7 +284,8 @@ def main():
         "passes": passes,
         "kernels": kernels,
         "roofline": {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak,
-                     "unit": unit, "frac": achieved / peak, "traffic": None},
+                     "unit": unit, "frac": achieved / peak,
+                     "traffic": profiled_traffic(w.name, dom)},
         "cpu_baseline": cpu,
     }
     if secondary:
