@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kMaxN = 1 << 24;
+constexpr int kMaxN = 1 << 23;  // one head's tensor stays below 4 GiB (buffer range)
 
 bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -104,6 +104,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
 
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave index as a scalar
   const int logical = xcd_logical_block(blockIdx.x, total);
   const int bh = logical / nkt;
   const int kt = logical - bh * nkt;  // causal: small kt has the most queries, runs first
@@ -112,43 +113,42 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int mykey = wk0 + l32;
 
   const size_t base = (size_t)bh * (size_t)N * D;
-  const uint16_t* Qh = Q + base;
-  const uint16_t* dOh = dO + base;
-  const float* LSEh = LSE + (size_t)bh * N;
-  const float* dlth = delta + (size_t)bh * N;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto rQ = make_rsrc(Q + base, head_bytes);
+  const auto rdO = make_rsrc(dO + base, head_bytes);
+  const auto rK = make_rsrc(K + base, head_bytes);
+  const auto rV = make_rsrc(V + base, head_bytes);
+  const auto rL = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
+  const auto rD = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
 
   // B operands of S = Q K^T and dP = dO V^T: lane holds row `mykey` of K, V.
   u32x4 kf[NDC], vf[NDC];
 #pragma unroll
   for (int cc = 0; cc < NDC; ++cc) {
-    const bool ok = mykey < N;
-    kf[cc] = ok ? ld_global16(K + base + (size_t)mykey * D + 16 * cc + 8 * hh) : zero4;
-    vf[cc] = ok ? ld_global16(V + base + (size_t)mykey * D + 16 * cc + 8 * hh) : zero4;
+    const uint32_t off = ((uint32_t)mykey * D + 16 * cc + 8 * hh) * 2u;
+    kf[cc] = buf_load16(rK, off);
+    vf[cc] = buf_load16(rV, off);
   }
 
   const int qstart = CAUSAL ? k0 : 0;  // earlier queries see none of these keys
   const int ntiles = qstart < N ? (N - qstart + BR - 1) / BR : 0;
 
-  // ---- staging: thread < 128 loads a 4x8 unit of Q, the rest of dO ----
-  const bool is_q = tid < 128;
+  // ---- staging: waves 0-1 load 4x8 units of Q, waves 2-3 of dO ----
+  const bool is_q = wave_u < 2;
   const int unit = tid & 127;
   const int ucc = unit % CPR, urg = unit / CPR;
-  const uint16_t* src = is_q ? Qh : dOh;
+  const auto rsrc = is_q ? rQ : rdO;
   u32x4 ur[4];
-  float sv = 0.f;
+  float lse_v = 0.f, dlt_v = 0.f;
   auto gload = [&](int qs) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int q = qs + 4 * urg + e;
-      ur[e] = q < N ? ld_global16(src + (size_t)q * D + ucc * 8) : zero4;
-    }
-    if (tid < 2 * BR) {
-      const int q = qs + (tid % BR);
-      if (tid < BR)  // LSE in log2 units; rows past N get +inf so P = 0
-        sv = q < N ? LSEh[q] * kLog2e : INFINITY;
-      else
-        sv = q < N ? dlth[q] : 0.f;
+    for (int e = 0; e < 4; ++e)
+      ur[e] = buf_load16(rsrc, ((uint32_t)(qs + 4 * urg + e) * D + ucc * 8) * 2u);
+    if (tid < BR) {
+      const int q = qs + tid;
+      // LSE in log2 units; rows past N get +inf so that their P is 0
+      lse_v = q < N ? buf_load_f32(rL, (uint32_t)q * 4u) * kLog2e : INFINITY;
+      dlt_v = buf_load_f32(rD, (uint32_t)q * 4u);
     }
   };
   const int upos = tposition(4 * urg);
@@ -159,7 +159,11 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int e = 0; e < 4; ++e) st_lds16(R + (4 * urg + e) * RST + ucc * 8, ur[e]);
     store_transposed4(Tt, TST, ucc * 8, upos, ur);
-    if (tid < 2 * BR) reinterpret_cast<float*>(S0 + STAGE16)[tid] = sv;
+    if (tid < BR) {
+      float* f = reinterpret_cast<float*>(S0 + STAGE16);
+      f[tid] = lse_v;
+      f[BR + tid] = dlt_v;
+    }
   };
 
   f32x16 dkacc[NDB], dvacc[NDB];
@@ -217,7 +221,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          float pv = exp2f(fmaf(s[r], c, -l4[e]));
+          float pv = fast_exp2(fmaf(s[r], c, -l4[e]));
           if (need_mask && qs + qo + e < mykey) pv = 0.f;
           p[e] = pv;
           ds[e] = pv * (dp[r] - d4[e]);
@@ -299,6 +303,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
 
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int logical = xcd_logical_block(blockIdx.x, total);
   const int bh = logical / nqt;
   int qt = logical - bh * nqt;
@@ -308,34 +313,37 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int myq = wq0 + l32;
 
   const size_t base = (size_t)bh * (size_t)N * D;
-  const uint16_t* Kh = K + base;
-  const uint16_t* Vh = V + base;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto rQ = make_rsrc(Q + base, head_bytes);
+  const auto rdO = make_rsrc(dO + base, head_bytes);
+  const auto rK = make_rsrc(K + base, head_bytes);
+  const auto rV = make_rsrc(V + base, head_bytes);
 
   u32x4 qf[NDC], gf[NDC];
 #pragma unroll
   for (int cc = 0; cc < NDC; ++cc) {
-    const bool ok = myq < N;
-    qf[cc] = ok ? ld_global16(Q + base + (size_t)myq * D + 16 * cc + 8 * hh) : zero4;
-    gf[cc] = ok ? ld_global16(dO + base + (size_t)myq * D + 16 * cc + 8 * hh) : zero4;
+    const uint32_t off = ((uint32_t)myq * D + 16 * cc + 8 * hh) * 2u;
+    qf[cc] = buf_load16(rQ, off);
+    gf[cc] = buf_load16(rdO, off);
   }
-  const float lse2 = myq < N ? LSE[(size_t)bh * N + myq] * kLog2e : 0.f;
-  const float dlt = myq < N ? delta[(size_t)bh * N + myq] : 0.f;
+  const auto rL = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
+  const auto rD = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
+  const float lse2 = buf_load_f32(rL, (uint32_t)myq * 4u) * kLog2e;
+  const float dlt = buf_load_f32(rD, (uint32_t)myq * 4u);
 
   const int kend = CAUSAL ? min(N, q0 + kDqBR) : N;
   const int ntiles = (kend + BC - 1) / BC;
 
-  const bool is_k = tid < 128;
+  // ---- staging: waves 0-1 load 4x8 units of K, waves 2-3 of V ----
+  const bool is_k = wave_u < 2;
   const int unit = tid & 127;
   const int ucc = unit % CPR, urg = unit / CPR;
-  const uint16_t* src = is_k ? Kh : Vh;
+  const auto rsrc = is_k ? rK : rV;
   u32x4 ur[4];
   auto gload = [&](int ts) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = ts + 4 * urg + e;
-      ur[e] = key < N ? ld_global16(src + (size_t)key * D + ucc * 8) : zero4;
-    }
+    for (int e = 0; e < 4; ++e)
+      ur[e] = buf_load16(rsrc, ((uint32_t)(ts + 4 * urg + e) * D + ucc * 8) * 2u);
   };
   const int upos = tposition(4 * urg);
   auto lstore = [&](int stage) {
@@ -389,7 +397,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
               const int r = 8 * half + 2 * i + e;
-              float pv = exp2f(fmaf(s[r], c, -lse2));
+              float pv = fast_exp2(fmaf(s[r], c, -lse2));
               if (need_mask) {
                 const int key = ts + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
                 if (key >= N || (CAUSAL && key > myq)) pv = 0.f;

@@ -62,9 +62,41 @@ struct F16 {
 };
 
 // ---- lane exchange ----
-// value held by lane l ^ 32 (the other half of the wave)
-__device__ inline float swap_halves(float x) {
-  return __shfl_xor(x, 32, 64);
+// Combine a value with the one held by lane l ^ 32 (the other wave half)
+// using v_permlane32_swap: after the swap one result register holds the
+// lower half twice and the other the upper half twice, so max/sum of the two
+// gives every lane the pairwise result whichever half the swap moves.
+__device__ inline float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 2^x on the transcendental unit (v_exp_f32).  Results below 2^-126 flush to
+// zero, which only drops softmax weights smaller than 1e-38 of the row max.
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// True on every lane when any lane of the wave has `pred` set.
+__device__ inline bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
+
+// ---- buffer loads ----
+// A raw buffer resource over one (batch, head) slab: loads whose byte offset
+// is at or past `bytes` return zeros instead of touching memory, which masks
+// ragged tails without branches.  Word 3 = 0x00020000 is the gfx9 data format
+// for untyped 32-bit dwords.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ inline float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
 }
 
 // ---- memory helpers ----

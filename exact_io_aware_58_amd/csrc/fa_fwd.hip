@@ -54,6 +54,7 @@ struct FwdTile<128> {
 };
 
 constexpr int kFwdBR = 128;  // query rows per workgroup (4 waves x 32)
+constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay <= 256
 
 template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2)
@@ -88,17 +89,16 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int myq = wq0 + l32;
 
   const size_t base = (size_t)bh * (size_t)N * D;
-  const uint16_t* Qh = Q + base;
-  const uint16_t* Kh = K + base;
-  const uint16_t* Vh = V + base;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto rQ = make_rsrc(Q + base, head_bytes);
+  const auto rK = make_rsrc(K + base, head_bytes);
+  const auto rV = make_rsrc(V + base, head_bytes);
 
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-
-  // B operand of S^T = K Q^T: lane (l32, hh) holds Q[myq][16c + 8hh .. +7].
+  // B operand of S^T = K Q^T: lane (l32, hh) holds Q[myq][16c + 8hh .. +7]
+  // (zeros past the last row).
   u32x4 qf[NDC];
 #pragma unroll
-  for (int cc = 0; cc < NDC; ++cc)
-    qf[cc] = myq < N ? ld_global16(Qh + (size_t)myq * D + 16 * cc + 8 * hh) : zero4;
+  for (int cc = 0; cc < NDC; ++cc) qf[cc] = buf_load16(rQ, ((uint32_t)myq * D + 16 * cc + 8 * hh) * 2u);
 
   const int kend = CAUSAL ? min(N, q0 + kFwdBR) : N;
   const int ntiles = (kend + BC - 1) / BC;
@@ -112,14 +112,11 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int j = 0; j < KCH; ++j) {
       const int id = j * 256 + tid;
       const int row = id / CPR, cc = id % CPR;
-      const int key = ts + row;
-      kr[j] = key < N ? ld_global16(Kh + (size_t)key * D + cc * 8) : zero4;
+      kr[j] = buf_load16(rK, ((uint32_t)(ts + row) * D + cc * 8) * 2u);
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = ts + 4 * vkg + e;
-      vr[e] = key < N ? ld_global16(Vh + (size_t)key * D + vcc * 8) : zero4;
-    }
+    for (int e = 0; e < 4; ++e)
+      vr[e] = buf_load16(rV, ((uint32_t)(ts + 4 * vkg + e) * D + vcc * 8) * 2u);
   };
   // V^T columns are stored in tposition() order, so the 8 consecutive
   // columns a lane reads for one PV step are exactly the keys whose
@@ -142,8 +139,13 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m = -INFINITY;  // running max of scale*log2(e)*s over this row
-  float lpart = 0.f;    // running sum over the keys this lane holds
+  // Reference maximum (log2 units) the exponents are taken against, and the
+  // partial row sum over the keys this lane holds.  The reference is only
+  // moved when a tile's maximum exceeds it by more than kRescaleSlack, so the
+  // rescale of O and l (exact in any case: O and l always share the
+  // reference) is rare; weights then stay below 2^kRescaleSlack.
+  float m = -INFINITY;
+  float lpart = 0.f;
 
   gload(0);
   lstore(0);
@@ -183,10 +185,17 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float mnew = fmaxf(m, mx * c);
-      const float alpha = exp2f(m - mnew);
-      m = mnew;
+      const float mt = max_halves(mx) * c;  // tile row max, log2 units
+      if (wave_any(mt > m + kRescaleSlack)) {
+        const float mnew = fmaxf(m, mt);
+        const float alpha = fast_exp2(m - mnew);  // 0 on the first tile
+        m = mnew;
+        lpart *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
 
       // P^T as the B operand of O^T += V^T P^T (registers 8*half .. +7 of
       // block kb are the 8 K-slots of reduction step 2*kb + half).
@@ -198,16 +207,12 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         for (int half = 0; half < 2; ++half)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float p0 = exp2f(fmaf(s[kb][8 * half + 2 * i], c, -mnew));
-            const float p1 = exp2f(fmaf(s[kb][8 * half + 2 * i + 1], c, -mnew));
+            const float p0 = fast_exp2(fmaf(s[kb][8 * half + 2 * i], c, -m));
+            const float p1 = fast_exp2(fmaf(s[kb][8 * half + 2 * i + 1], c, -m));
             rs += p0 + p1;
             pk[2 * kb + half][i] = T::pack2(p0, p1);
           }
-      lpart = lpart * alpha + rs;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      lpart += rs;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -221,7 +226,7 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 
   // Epilogue: one division by the full row sum, then bf16/f16 (RNE) stores.
-  const float ltot = lpart + swap_halves(lpart);
+  const float ltot = sum_halves(lpart);
   const float inv = 1.f / ltot;
   if (myq < N) {
     uint16_t* Oq = O + base + (size_t)myq * D;
@@ -303,14 +308,14 @@ fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
       mx = fmaxf(mx, acc);
     }
     const float mnew = fmaxf(m, mx * c);
-    const float alpha = exp2f(m - mnew);
+    const float alpha = fast_exp2(m - mnew);
     m = mnew;
     l *= alpha;
 #pragma unroll
     for (int e = 0; e < DP; ++e) o[e] *= alpha;
 #pragma unroll
     for (int j = 0; j < BK; ++j) {
-      const float p = exp2f(fmaf(s[j], c, -mnew));
+      const float p = fast_exp2(fmaf(s[j], c, -mnew));
       l += p;
 #pragma unroll
       for (int e = 0; e < DP; ++e) o[e] = fmaf(p, Vs[j * D + part * DP + e], o[e]);

@@ -47,7 +47,7 @@ typedef enum {
 
 typedef enum {
   FA_OK = 0,
-  FA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, B/H/N <= 0, size overflow, bad scale */
+  FA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, B/H/N <= 0, N > 2^23, bad scale        */
   FA_ERR_UNSUPPORTED = -2,  /* D not in {64, 128} or unknown dtype                         */
   FA_ERR_WORKSPACE = -3,    /* backward workspace missing or smaller than required          */
   FA_ERR_HIP = -4           /* a kernel launch failed (hipGetLastError after the launch)    */
@@ -66,7 +66,7 @@ typedef enum {
  *   LSE     : [B, H, N] float32, written: LSE_i = m_i + ln(l_i), the natural
  *             log of row i's softmax normaliser of the scaled, masked scores.
  *             The backward pass reads it to recompute P.
- *   D       : 64 or 128.  Any N >= 1 (ragged tails are masked).
+ *   D       : 64 or 128.  1 <= N <= 2^23 (ragged tails are masked).
  * Returns an fa_status.
  */
 int fa_fwd(int dtype, int B, int H, int N, int D, float scale, int causal,
