@@ -68,7 +68,7 @@ extern "C" int fa_fwd(int dtype, int B, int H, int N, int D, float scale, int ca
 extern "C" size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int D, int causal) {
   (void)causal;
   if (dtype == FA_F32 || check_problem(dtype, B, H, N, D, 1.f) != FA_OK) return 0;
-  return delta_bytes(B, H, N);
+  return 2 * delta_bytes(B, H, N);
 }
 
 extern "C" int fa_bwd(int dtype, int B, int H, int N, int D, float scale, int causal,
@@ -81,10 +81,13 @@ extern "C" int fa_bwd(int dtype, int B, int H, int N, int D, float scale, int ca
   const void* ptrs[] = {Q, K, V, O, dO, LSE, dQ, dK, dV};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < delta_bytes(B, H, N)) return FA_ERR_WORKSPACE;
+  const size_t rows_bytes = delta_bytes(B, H, N);
+  if (!workspace || workspace_bytes < 2 * rows_bytes) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
+  float* delta = (float*)workspace;
+  float* lse2 = (float*)((char*)workspace + rows_bytes);
   fa::BwdArgs a{dtype, B, H, N, D, scale, causal ? 1 : 0, Q, K, V, O, dO, LSE,
-                dQ, dK, dV, (float*)workspace, (hipStream_t)stream};
+                dQ, dK, dV, delta, lse2, (hipStream_t)stream};
   hipError_t e;
   {
     fa::TimedLaunch t(FA_KERNEL_BWD_DELTA, a.stream);

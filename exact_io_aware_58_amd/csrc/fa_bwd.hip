@@ -17,17 +17,20 @@
 //   dS = P * (dP - Delta),  dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Three kernels, no atomics (bit-for-bit repeatable):
-//   1. delta: Delta_i = dO_i . O_i, float32, into the caller's workspace.
+//   1. delta: Delta_i = dO_i . O_i and LSE_i * log2(e), float32, into the
+//             caller's workspace.
 //   2. dkdv:  a workgroup keeps 128 key rows resident (each wave 32 keys, K and
 //             V as VGPR operands, dK^T and dV^T accumulators in VGPRs) and
-//             streams query tiles (Q, dO row-major and transposed, LSE, Delta)
-//             through double-buffered LDS.  Per 32x32 block: S = Q K^T and
+//             streams query tiles (Q, dO, LSE, Delta) into double-buffered LDS
+//             with direct global->LDS loads.  Per 32x32 block: S = Q K^T and
 //             dP = dO V^T leave one key per lane, so P and dS feed straight in
-//             as B operands of dV^T += dO^T P and dK^T += Q^T dS.
+//             as B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A
+//             operands come from the same row-major Q and dO tiles through
+//             transposing LDS reads.
 //   3. dq:    a workgroup keeps 128 query rows resident (Q, dO as operands,
-//             LSE and Delta one scalar per lane) and streams key tiles (K, V
-//             row-major, K transposed).  S^T = K Q^T and dP^T = V dO^T leave
-//             one query per lane, so dS^T feeds dQ^T += K^T dS^T directly.
+//             LSE and Delta one scalar per lane) and streams key tiles (K, V).
+//             S^T = K Q^T and dP^T = V dO^T leave one query per lane, so dS^T
+//             feeds dQ^T += K^T dS^T directly (K^T by transposing reads).
 // The dq kernel recomputes S and dP a second time; that costs two extra
 // contractions per tile but removes every cross-workgroup reduction.
 #include <hip/hip_runtime.h>
@@ -41,10 +44,12 @@ namespace fa {
 
 // ------------------------------------------------------------------ delta
 
+// Delta_i = dO_i . O_i (fp32) and LSE_i * log2(e), one row per D/8 lanes.
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 bwd_delta_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-                 float* __restrict__ delta, size_t rows) {
+                 const float* __restrict__ LSE, float* __restrict__ delta,
+                 float* __restrict__ lse2, size_t rows) {
   constexpr int TPR = D / 8;  // threads per row, 16 bytes each
   constexpr int RPB = 256 / TPR;
   const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / TPR;
@@ -58,7 +63,10 @@ bwd_delta_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && part == 0) delta[row] = acc;
+  if (row < rows && part == 0) {
+    delta[row] = acc;
+    lse2[row] = LSE[row] * kLog2e;
+  }
 }
 
 // ------------------------------------------------------------------ dK, dV
@@ -67,7 +75,7 @@ template <int D>
 struct DkvTile;
 template <>
 struct DkvTile<64> {
-  static constexpr int BR = 64;   // query rows per streamed tile
+  static constexpr int BR = 64;     // query rows per streamed tile
   static constexpr int MIN_WG = 2;  // workgroups per CU the registers must allow
 };
 template <>
@@ -82,29 +90,27 @@ template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, DkvTile<D>::MIN_WG)
 bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                const float* __restrict__ LSE, const float* __restrict__ delta,
+                const float* __restrict__ lse2, const float* __restrict__ delta,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, float c,
                 float scale, int nkt, int total) {
   constexpr int BR = DkvTile<D>::BR;
-  constexpr int RST = D + 8;   // row-major tile stride
-  constexpr int TST = BR + 8;  // transposed tile stride
-  constexpr int RELEMS = BR * RST;
-  constexpr int TELEMS = D * TST;
-  constexpr int STAGE16 = 2 * RELEMS + 2 * TELEMS;        // Q, dO, Q^T, dO^T
-  constexpr int STAGE = STAGE16 + 2 * BR * 2;              // + LSE2, Delta (fp32)
-  constexpr int CPR = D / 8;
-  constexpr int UNITS = BR * D / 32;  // 4-row x 8-column units per tensor
+  constexpr int TILE = BR * D;                  // elements of one Q or dO tile
+  constexpr int BLOCKS = TILE * 2 / 1024;       // 1 KiB blocks per tile
+  constexpr int STAGE = 2 * TILE + 2 * 64 * 2;  // Q, dO, then 64 LSE2 + 64 Delta floats
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
-  static_assert(UNITS == 128, "one unit per thread, Q on threads 0-127, dO on 128-255");
+  static_assert(BLOCKS == 8, "two blocks of Q and two of dO per wave");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  // Two stages in separate arrays, the loop unrolled by two: loads into one
+  // stage provably never alias reads of the other (no spurious waits).
+  __shared__ __attribute__((aligned(1024))) uint16_t smem0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem1[STAGE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int l32 = lane & 31, hh = lane >> 5;
 
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave index as a scalar
   const int logical = xcd_logical_block(blockIdx.x, total);
   const int bh = logical / nkt;
   const int kt = logical - bh * nkt;  // causal: small kt has the most queries, runs first
@@ -118,7 +124,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const auto rdO = make_rsrc(dO + base, head_bytes);
   const auto rK = make_rsrc(K + base, head_bytes);
   const auto rV = make_rsrc(V + base, head_bytes);
-  const auto rL = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
+  const auto rL = make_rsrc(lse2 + (size_t)bh * N, (uint32_t)N * 4);
   const auto rD = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
 
   // B operands of S = Q K^T and dP = dO V^T: lane holds row `mykey` of K, V.
@@ -130,40 +136,40 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     vf[cc] = buf_load16(rV, off);
   }
 
+  // Per-lane LDS offsets.  Row-major operands (S and dP): query row l32 of a
+  // 32-row block, columns 16cc + 8hh.  Transposed operands (Q^T, dO^T for
+  // dK^T, dV^T): as for the forward kernel's V^T reads, with queries as rows.
+  int roff[NDC];
+#pragma unroll
+  for (int cc = 0; cc < NDC; ++cc) roff[cc] = toff<D>(l32, 16 * cc + 8 * hh);
+  const int G = lane >> 4, a16 = lane & 15;
+  int toffs[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      toffs[db][t] = toff<D>(8 * t + 4 * (G >> 1) + (a16 >> 2), 32 * db + 16 * (G & 1) + 4 * (a16 & 3));
+
   const int qstart = CAUSAL ? k0 : 0;  // earlier queries see none of these keys
   const int ntiles = qstart < N ? (N - qstart + BR - 1) / BR : 0;
 
-  // ---- staging: waves 0-1 load 4x8 units of Q, waves 2-3 of dO ----
-  const bool is_q = wave_u < 2;
-  const int unit = tid & 127;
-  const int ucc = unit % CPR, urg = unit / CPR;
-  const auto rsrc = is_q ? rQ : rdO;
-  u32x4 ur[4];
-  float lse_v = 0.f, dlt_v = 0.f;
-  auto gload = [&](int qs) {
+  // Direct global->LDS loads of one query tile: each wave two blocks of Q and
+  // two of dO; wave 0 also 64 LSE2 values, wave 1 64 Delta values.  Rows
+  // past N arrive as zeros (then P = 1 but dO = Q = 0: no contribution).
+  auto dma = [&](const uint16_t* S0, int qs) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      ur[e] = buf_load16(rsrc, ((uint32_t)(qs + 4 * urg + e) * D + ucc * 8) * 2u);
-    if (tid < BR) {
-      const int q = qs + tid;
-      // LSE in log2 units; rows past N get +inf so that their P is 0
-      lse_v = q < N ? buf_load_f32(rL, (uint32_t)q * 4u) * kLog2e : INFINITY;
-      dlt_v = buf_load_f32(rD, (uint32_t)q * 4u);
+    for (int i = 0; i < BLOCKS / 4; ++i) {
+      const int b = wave_u + 4 * i;
+      const uint32_t goff = dma_goff<D>(b, lane, qs);
+      lds_dma16(rQ, S0 + b * 512, goff);
+      lds_dma16(rdO, S0 + TILE + b * 512, goff);
     }
-  };
-  const int upos = tposition(4 * urg);
-  auto lstore = [&](int stage) {
-    uint16_t* S0 = smem + stage * STAGE;
-    uint16_t* R = S0 + (is_q ? 0 : RELEMS);
-    uint16_t* Tt = S0 + 2 * RELEMS + (is_q ? 0 : TELEMS);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) st_lds16(R + (4 * urg + e) * RST + ucc * 8, ur[e]);
-    store_transposed4(Tt, TST, ucc * 8, upos, ur);
-    if (tid < BR) {
-      float* f = reinterpret_cast<float*>(S0 + STAGE16);
-      f[tid] = lse_v;
-      f[BR + tid] = dlt_v;
-    }
+    if (wave_u == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, to_lds(S0 + 2 * TILE), 4,
+                                               (uint32_t)(qs + lane) * 4u, 0, 0, 0);
+    else if (wave_u == 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, to_lds(S0 + 2 * TILE + 128), 4,
+                                               (uint32_t)(qs + lane) * 4u, 0, 0, 0);
   };
 
   f32x16 dkacc[NDB], dvacc[NDB];
@@ -175,23 +181,11 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       dvacc[db][r] = 0.f;
     }
 
-  if (ntiles > 0) {
-    gload(qstart);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int qs = qstart + t * BR;
-    if (t + 1 < ntiles) gload(qs + BR);
-    const uint16_t* S0 = smem + (t & 1) * STAGE;
+  auto tile = [&](const uint16_t* S0, int qs) {
     const uint16_t* Qs = S0;
-    const uint16_t* dOs = S0 + RELEMS;
-    const uint16_t* Qt = S0 + 2 * RELEMS;
-    const uint16_t* dOt = Qt + TELEMS;
-    const float* lse2s = reinterpret_cast<const float*>(S0 + STAGE16);
-    const float* dlts = lse2s + BR;
-
+    const uint16_t* dOs = S0 + TILE;
+    const float* lse2s = reinterpret_cast<const float*>(S0 + 2 * TILE);
+    const float* dlts = lse2s + 64;
 #pragma unroll
     for (int qb = 0; qb < BR / 32; ++qb) {
       const int qb0 = qs + qb * 32;
@@ -204,10 +198,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       }
 #pragma unroll
       for (int cc = 0; cc < NDC; ++cc) {
-        const u32x4 aq = ld_lds16(Qs + (qb * 32 + l32) * RST + 16 * cc + 8 * hh);
-        s = T::mfma(aq, kf[cc], s);
-        const u32x4 ag = ld_lds16(dOs + (qb * 32 + l32) * RST + 16 * cc + 8 * hh);
-        dp = T::mfma(ag, vf[cc], dp);
+        s = T::mfma(ld_lds16(Qs + qb * 32 * D + roff[cc]), kf[cc], s);
+        dp = T::mfma(ld_lds16(dOs + qb * 32 * D + roff[cc]), vf[cc], dp);
       }
       // lane: key `mykey`; register r: query qb0 + 8*(r/4) + 4*hh + r%4
       const bool need_mask = CAUSAL && qb0 < wk0 + 31;
@@ -235,12 +227,29 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int qc = 0; qc < 2; ++qc) {
-          const int off = (db * 32 + l32) * TST + qb * 32 + 16 * qc + 8 * hh;
-          dvacc[db] = T::mfma(ld_lds16(dOt + off), pp[qc], dvacc[db]);
-          dkacc[db] = T::mfma(ld_lds16(Qt + off), dsp[qc], dkacc[db]);
+          const int rb = (qb * 32 + qc * 16) * D;
+          const u32x4 ag =
+              cat(ld_lds_tr(dOs + rb + toffs[db][0]), ld_lds_tr(dOs + rb + toffs[db][1]));
+          dvacc[db] = T::mfma(ag, pp[qc], dvacc[db]);
+          const u32x4 aq =
+              cat(ld_lds_tr(Qs + rb + toffs[db][0]), ld_lds_tr(Qs + rb + toffs[db][1]));
+          dkacc[db] = T::mfma(aq, dsp[qc], dkacc[db]);
         }
     }
-    if (t + 1 < ntiles) lstore((t + 1) & 1);
+  };
+
+  if (ntiles > 0) dma(smem0, qstart);
+  wait_dma();
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    if (t + 1 < ntiles) dma(smem1, qstart + (t + 1) * BR);
+    tile(smem0, qstart + t * BR);
+    wait_dma();
+    __syncthreads();
+    if (t + 1 >= ntiles) break;
+    if (t + 2 < ntiles) dma(smem0, qstart + (t + 2) * BR);
+    tile(smem1, qstart + (t + 1) * BR);
+    wait_dma();
     __syncthreads();
   }
 
@@ -282,28 +291,25 @@ template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-              const float* __restrict__ LSE, const float* __restrict__ delta,
+              const float* __restrict__ lse2g, const float* __restrict__ delta,
               uint16_t* __restrict__ dQ, int N, float c, float scale, int nqt, int total) {
   constexpr int BC = DqTile<D>::BC;
-  constexpr int RST = D + 8;
-  constexpr int TST = BC + 8;
-  constexpr int RELEMS = BC * RST;
-  constexpr int STAGE = 2 * RELEMS + D * TST;  // K, V row-major; K^T
-  constexpr int CPR = D / 8;
-  constexpr int UNITS = BC * D / 32;
+  constexpr int TILE = BC * D;             // elements of one K or V tile
+  constexpr int BLOCKS = TILE * 2 / 1024;  // 1 KiB blocks per tile
   constexpr int NKB = BC / 32;
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
   constexpr int NKC = BC / 16;
-  static_assert(UNITS == 128, "one unit per thread, K on threads 0-127, V on 128-255");
+  static_assert(BLOCKS == 8, "two blocks of K and two of V per wave");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem1[2 * TILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int l32 = lane & 31, hh = lane >> 5;
 
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int logical = xcd_logical_block(blockIdx.x, total);
   const int bh = logical / nqt;
   int qt = logical - bh * nqt;
@@ -326,32 +332,33 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     qf[cc] = buf_load16(rQ, off);
     gf[cc] = buf_load16(rdO, off);
   }
-  const auto rL = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
+  const auto rL = make_rsrc(lse2g + (size_t)bh * N, (uint32_t)N * 4);
   const auto rD = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
-  const float lse2 = buf_load_f32(rL, (uint32_t)myq * 4u) * kLog2e;
+  const float lse2 = buf_load_f32(rL, (uint32_t)myq * 4u);
   const float dlt = buf_load_f32(rD, (uint32_t)myq * 4u);
+
+  int roff[NDC];
+#pragma unroll
+  for (int cc = 0; cc < NDC; ++cc) roff[cc] = toff<D>(l32, 16 * cc + 8 * hh);
+  const int G = lane >> 4, a16 = lane & 15;
+  int toffs[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      toffs[db][t] = toff<D>(8 * t + 4 * (G >> 1) + (a16 >> 2), 32 * db + 16 * (G & 1) + 4 * (a16 & 3));
 
   const int kend = CAUSAL ? min(N, q0 + kDqBR) : N;
   const int ntiles = (kend + BC - 1) / BC;
 
-  // ---- staging: waves 0-1 load 4x8 units of K, waves 2-3 of V ----
-  const bool is_k = wave_u < 2;
-  const int unit = tid & 127;
-  const int ucc = unit % CPR, urg = unit / CPR;
-  const auto rsrc = is_k ? rK : rV;
-  u32x4 ur[4];
-  auto gload = [&](int ts) {
+  auto dma = [&](const uint16_t* S0, int ts) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      ur[e] = buf_load16(rsrc, ((uint32_t)(ts + 4 * urg + e) * D + ucc * 8) * 2u);
-  };
-  const int upos = tposition(4 * urg);
-  auto lstore = [&](int stage) {
-    uint16_t* S0 = smem + stage * STAGE;
-    uint16_t* R = S0 + (is_k ? 0 : RELEMS);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) st_lds16(R + (4 * urg + e) * RST + ucc * 8, ur[e]);
-    if (is_k) store_transposed4(S0 + 2 * RELEMS, TST, ucc * 8, upos, ur);
+    for (int i = 0; i < BLOCKS / 4; ++i) {
+      const int b = wave_u + 4 * i;
+      const uint32_t goff = dma_goff<D>(b, lane, ts);
+      lds_dma16(rK, S0 + b * 512, goff);
+      lds_dma16(rV, S0 + TILE + b * 512, goff);
+    }
   };
 
   f32x16 acc[NDB];
@@ -360,17 +367,9 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int ts = t * BC;
-    if (t + 1 < ntiles) gload(ts + BC);
-    const uint16_t* Ks = smem + (t & 1) * STAGE;
-    const uint16_t* Vs = Ks + RELEMS;
-    const uint16_t* Kt = Ks + 2 * RELEMS;
-
+  auto tile = [&](const uint16_t* S0, int ts) {
+    const uint16_t* Ks = S0;
+    const uint16_t* Vs = S0 + TILE;
     if (!CAUSAL || ts <= wq0 + 31) {
       const bool need_mask = (ts + BC > N) || (CAUSAL && ts + BC - 1 > wq0);
       u32x4 dsk[NKC];
@@ -384,9 +383,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         }
 #pragma unroll
         for (int cc = 0; cc < NDC; ++cc) {
-          const int off = (kb * 32 + l32) * RST + 16 * cc + 8 * hh;
-          s = T::mfma(ld_lds16(Ks + off), qf[cc], s);
-          dp = T::mfma(ld_lds16(Vs + off), gf[cc], dp);
+          s = T::mfma(ld_lds16(Ks + kb * 32 * D + roff[cc]), qf[cc], s);
+          dp = T::mfma(ld_lds16(Vs + kb * 32 * D + roff[cc]), gf[cc], dp);
         }
         // lane: query `myq`; register r: key ts + kb*32 + 8*(r/4) + 4*hh + r%4
 #pragma unroll
@@ -411,11 +409,25 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
-          const u32x4 a = ld_lds16(Kt + (db * 32 + l32) * TST + 16 * kc + 8 * hh);
+          const uint16_t* kb16 = Ks + kc * 16 * D;
+          const u32x4 a = cat(ld_lds_tr(kb16 + toffs[db][0]), ld_lds_tr(kb16 + toffs[db][1]));
           acc[db] = T::mfma(a, dsk[kc], acc[db]);
         }
     }
-    if (t + 1 < ntiles) lstore((t + 1) & 1);
+  };
+
+  dma(smem0, 0);
+  wait_dma();
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    if (t + 1 < ntiles) dma(smem1, (t + 1) * BC);
+    tile(smem0, t * BC);
+    wait_dma();
+    __syncthreads();
+    if (t + 1 >= ntiles) break;
+    if (t + 2 < ntiles) dma(smem0, (t + 2) * BC);
+    tile(smem1, (t + 1) * BC);
+    wait_dma();
     __syncthreads();
   }
 
@@ -442,10 +454,10 @@ static hipError_t delta16(const BwdArgs& a) {
   const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
   if (a.D == 64)
     hipLaunchKernelGGL((bwd_delta_kernel<T, 64>), dim3(grid), dim3(256), 0, a.stream,
-                       (const uint16_t*)a.O, (const uint16_t*)a.dO, a.delta, rows);
+                       (const uint16_t*)a.O, (const uint16_t*)a.dO, a.LSE, a.delta, a.lse2, rows);
   else
     hipLaunchKernelGGL((bwd_delta_kernel<T, 128>), dim3(grid), dim3(256), 0, a.stream,
-                       (const uint16_t*)a.O, (const uint16_t*)a.dO, a.delta, rows);
+                       (const uint16_t*)a.O, (const uint16_t*)a.dO, a.LSE, a.delta, a.lse2, rows);
   return hipGetLastError();
 }
 
@@ -459,7 +471,7 @@ static hipError_t dkdv(const BwdArgs& a) {
   const int total = nkt * a.B * a.H;
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
                      (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                     (const uint16_t*)a.dO, a.LSE, a.delta, (uint16_t*)a.dK, (uint16_t*)a.dV,
+                     (const uint16_t*)a.dO, a.lse2, a.delta, (uint16_t*)a.dK, (uint16_t*)a.dV,
                      a.N, a.scale * kLog2e, a.scale, nkt, total);
   return hipGetLastError();
 }
@@ -480,7 +492,7 @@ static hipError_t dq(const BwdArgs& a) {
   const int total = nqt * a.B * a.H;
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
                      (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                     (const uint16_t*)a.dO, a.LSE, a.delta, (uint16_t*)a.dQ, a.N,
+                     (const uint16_t*)a.dO, a.lse2, a.delta, (uint16_t*)a.dQ, a.N,
                      a.scale * kLog2e, a.scale, nqt, total);
   return hipGetLastError();
 }

@@ -122,6 +122,72 @@ __device__ inline uint32_t elem16(u32x4 v, int j) {
   return (j & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
+// ---- swizzled row-major LDS tiles ----
+// A tile of rows of D 16-bit elements is stored densely (row stride D), with
+// the 16-byte chunk c of row r placed at chunk position c ^ g(r).  gfx950 LDS
+// has 64 banks of 4 bytes (256 bytes per cycle).  g is chosen so that
+//  * 16 lanes reading the same chunk of 16 consecutive rows (a 16-byte MFMA
+//    operand read, one row per lane) hit 16 distinct 16-byte bank groups, and
+//  * the 32 lanes of a transposing read (ds_read_b64_tr_b16: 4 consecutive
+//    rows x 64 aligned bytes each) cover all 256 bytes of the banks once;
+// both are conflict-free.  g only uses row bits 0..3, so a row offset that is
+// a multiple of 16 leaves the swizzle unchanged (offsets stay additive).
+// The layout is dense in 1 KiB blocks, which is what the direct
+// global->LDS loads write (64 lanes x 16 bytes, lane l at byte 16*l).
+template <int D>
+struct Swz;
+template <>
+struct Swz<128> {  // 16 chunks per 256-byte row
+  __device__ static inline int g(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+};
+template <>
+struct Swz<64> {  // 8 chunks per 128-byte row, two rows per bank cycle
+  __device__ static inline int g(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+};
+// element offset of (row r, column col) inside a swizzled tile
+template <int D>
+__device__ inline int toff(int r, int col) {
+  return r * D + (((col >> 3) ^ Swz<D>::g(r)) << 3) + (col & 7);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ inline lds_void* to_lds(const void* p) {
+  return (lds_void*)((__attribute__((address_space(3))) char*)(p));
+}
+
+// One 1 KiB block of a swizzled tile straight from global memory into LDS:
+// lane l fetches 16 bytes at byte offset `goff` of the buffer `r` and the
+// hardware writes them to lds_block + 16*l (lds_block is wave-uniform).
+// Offsets past the buffer's end write zeros.
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, const uint16_t* lds_block, uint32_t goff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(lds_block), 16, goff, 0, 0, 0);
+}
+
+// Global byte offset lane `lane` must fetch for 1 KiB block `b` of a tile
+// whose first row is global row `row0`.
+template <int D>
+__device__ inline uint32_t dma_goff(int b, int lane, int row0) {
+  constexpr int CPR = D / 8, RPB = 512 / D;
+  const int row = b * RPB + lane / CPR;
+  const int chunk = (lane % CPR) ^ Swz<D>::g(row);
+  return ((uint32_t)(row0 + row) * D + chunk * 8) * 2u;
+}
+
+// Wait until this wave's direct-to-LDS loads have landed (vmcnt = 0).
+__device__ inline void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// 64-bit transposing LDS read: within each 16-lane group, lane j receives
+// element j%4 of the 8-byte chunks addressed by lanes j/4, 4+j/4, 8+j/4 and
+// 12+j/4 (one element from each of four rows).
+__device__ inline u32x2 ld_lds_tr(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)to_lds(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+__device__ inline u32x4 cat(u32x2 lo, u32x2 hi) { return u32x4{lo[0], lo[1], hi[0], hi[1]}; }
+
 // ---- transposed tile staging ----
 // Position of key (or query) row `row` (a multiple of 4) inside a transposed
 // LDS tile.  Inside every 16-row chunk the four 4-row groups {0,1,2,3} are

@@ -62,22 +62,24 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
              const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
              float* __restrict__ LSE, int N, float c, int nqt, int total) {
   constexpr int BC = FwdTile<D>::BC;
-  constexpr int KST = D + 8;   // LDS row stride of the K tile (elements)
-  constexpr int VST = BC + 8;  // LDS row stride of the V^T tile
-  constexpr int KELEMS = BC * KST;
-  constexpr int STAGE = KELEMS + D * VST;
-  constexpr int CPR = D / 8;            // 16-byte chunks per global row
-  constexpr int KCH = BC * CPR / 256;   // K chunks loaded per thread
-  constexpr int NKB = BC / 32;          // 32-key blocks per tile
-  constexpr int NDC = D / 16;           // reduction steps of S^T = K Q^T
-  constexpr int NDB = D / 32;           // 32-row blocks of O^T
-  constexpr int NKC = BC / 16;          // reduction steps of O^T += V^T P^T
-  static_assert(BC * D / 32 == 256, "one 4-key x 8-column V unit per thread");
+  constexpr int TILE = BC * D;             // elements of one K or V tile
+  constexpr int BLOCKS = TILE * 2 / 1024;  // 1 KiB blocks per tile
+  constexpr int NKB = BC / 32;             // 32-key blocks per tile
+  constexpr int NDC = D / 16;              // reduction steps of S^T = K Q^T
+  constexpr int NDB = D / 32;              // 32-row blocks of O^T
+  constexpr int NKC = BC / 16;             // reduction steps of O^T += V^T P^T
+  static_assert(BLOCKS % 4 == 0, "blocks split evenly over 4 waves");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  // Two stages, each a K tile then a V tile, both row-major and swizzled.
+  // Separate arrays (and a loop unrolled by two) let the compiler see that
+  // the loads into one stage never alias the reads of the other, so it does
+  // not wait for the prefetch before reading the current tile.
+  __shared__ __attribute__((aligned(1024))) uint16_t smem0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem1[2 * TILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int l32 = lane & 31, hh = lane >> 5;
 
   const int logical = xcd_logical_block(blockIdx.x, total);
@@ -100,38 +102,36 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
   for (int cc = 0; cc < NDC; ++cc) qf[cc] = buf_load16(rQ, ((uint32_t)myq * D + 16 * cc + 8 * hh) * 2u);
 
+  // Per-lane LDS offsets (elements).  K operand: row l32 of a 32-key block,
+  // columns 16cc + 8hh.  V^T operand via transposing reads: for d-block db
+  // and half t, this lane addresses key row 8t + 4*(lane/32) + (lane%16)/4
+  // of a 16-key chunk and d column 32db + 16*((lane/16)%2) + 4*(lane%4);
+  // the read hands every lane d column 32db + lane%32 of keys
+  // 16kc + 8t + 4*(lane/32) + {0,1,2,3}, exactly the keys whose P values sit
+  // in its S^T accumulator registers 8*(kc%2) + 4t .. +3.
+  int koff[NDC];
+#pragma unroll
+  for (int cc = 0; cc < NDC; ++cc) koff[cc] = toff<D>(l32, 16 * cc + 8 * hh);
+  const int G = lane >> 4, a16 = lane & 15;
+  int voff[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      voff[db][t] = toff<D>(8 * t + 4 * (G >> 1) + (a16 >> 2), 32 * db + 16 * (G & 1) + 4 * (a16 & 3));
+
   const int kend = CAUSAL ? min(N, q0 + kFwdBR) : N;
   const int ntiles = (kend + BC - 1) / BC;
 
-  // ---- tile staging: global -> registers -> LDS ----
-  u32x4 kr[KCH], vr[4];
-  const int vcc = tid % CPR;  // this thread's V column chunk
-  const int vkg = tid / CPR;  // this thread's V 4-key group
-  auto gload = [&](int ts) {
+  // Direct global->LDS loads of one key tile into a stage (K then V).
+  auto dma = [&](const uint16_t* Ks, int ts) {
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int id = j * 256 + tid;
-      const int row = id / CPR, cc = id % CPR;
-      kr[j] = buf_load16(rK, ((uint32_t)(ts + row) * D + cc * 8) * 2u);
+    for (int i = 0; i < BLOCKS / 4; ++i) {
+      const int b = wave_u + 4 * i;
+      const uint32_t goff = dma_goff<D>(b, lane, ts);
+      lds_dma16(rK, Ks + b * 512, goff);
+      lds_dma16(rV, Ks + TILE + b * 512, goff);
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      vr[e] = buf_load16(rV, ((uint32_t)(ts + 4 * vkg + e) * D + vcc * 8) * 2u);
-  };
-  // V^T columns are stored in tposition() order, so the 8 consecutive
-  // columns a lane reads for one PV step are exactly the keys whose
-  // probabilities sit in its 8 consecutive S^T accumulator registers.
-  const int vpos = tposition(4 * vkg);
-  auto lstore = [&](int stage) {
-    uint16_t* Ks = smem + stage * STAGE;
-    uint16_t* Vt = Ks + KELEMS;
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int id = j * 256 + tid;
-      const int row = id / CPR, cc = id % CPR;
-      st_lds16(Ks + row * KST + cc * 8, kr[j]);
-    }
-    store_transposed4(Vt, VST, vcc * 8, vpos, vr);
   };
 
   f32x16 oacc[NDB];
@@ -147,16 +147,8 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   float m = -INFINITY;
   float lpart = 0.f;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int ts = t * BC;
-    if (t + 1 < ntiles) gload(ts + BC);
-    const uint16_t* Ks = smem + (t & 1) * STAGE;
-    const uint16_t* Vt = Ks + KELEMS;
-
+  auto tile = [&](const uint16_t* Ks, int ts) {
+    const uint16_t* Vs = Ks + TILE;
     if (!CAUSAL || ts <= wq0 + 31) {
       // S^T[key][q] for the wave's 32 queries and the tile's BC keys.
       f32x16 s[NKB];
@@ -165,10 +157,8 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < NDC; ++cc) {
-          const u32x4 a = ld_lds16(Ks + (kb * 32 + l32) * KST + 16 * cc + 8 * hh);
-          s[kb] = T::mfma(a, qf[cc], s[kb]);
-        }
+        for (int cc = 0; cc < NDC; ++cc)
+          s[kb] = T::mfma(ld_lds16(Ks + kb * 32 * D + koff[cc]), qf[cc], s[kb]);
       }
       const bool need_mask = (ts + BC > N) || (CAUSAL && ts + BC - 1 > wq0);
       if (need_mask) {
@@ -217,11 +207,26 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
-          const u32x4 a = ld_lds16(Vt + (db * 32 + l32) * VST + 16 * kc + 8 * hh);
+          const uint16_t* vb = Vs + kc * 16 * D;
+          const u32x4 a = cat(ld_lds_tr(vb + voff[db][0]), ld_lds_tr(vb + voff[db][1]));
           oacc[db] = T::mfma(a, pk[kc], oacc[db]);
         }
     }
-    if (t + 1 < ntiles) lstore((t + 1) & 1);
+  };
+
+  dma(smem0, 0);
+  wait_dma();
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    // even tile in stage 0 while the odd one lands in stage 1, then swap
+    if (t + 1 < ntiles) dma(smem1, (t + 1) * BC);
+    tile(smem0, t * BC);
+    wait_dma();
+    __syncthreads();
+    if (t + 1 >= ntiles) break;
+    if (t + 2 < ntiles) dma(smem0, (t + 2) * BC);
+    tile(smem1, (t + 1) * BC);
+    wait_dma();
     __syncthreads();
   }
 

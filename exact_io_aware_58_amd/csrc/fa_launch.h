@@ -26,7 +26,8 @@ struct BwdArgs {
   const void *Q, *K, *V, *O, *dO;
   const float* LSE;
   void *dQ, *dK, *dV;
-  float* delta;  // [B, H, N] float32 scratch inside the caller's workspace
+  float* delta;  // [B, H, N] float32 in the caller's workspace: dO_i . O_i
+  float* lse2;   // [B, H, N] float32 in the caller's workspace: LSE_i * log2(e)
   hipStream_t stream;
 };
 

@@ -85,8 +85,8 @@ def test_fwd_rejects_null_or_misaligned(fa, which, bad):
 
 
 def test_workspace_bytes(fa):
-    assert fa.fa_bwd_workspace_bytes(fa.FA_BF16, 8, 12, 1024, 64, 1) == 8 * 12 * 1024 * 4
-    assert fa.fa_bwd_workspace_bytes(fa.FA_BF16, 1, 1, 3, 64, 0) == 256  # padded
+    assert fa.fa_bwd_workspace_bytes(fa.FA_BF16, 8, 12, 1024, 64, 1) == 2 * 8 * 12 * 1024 * 4
+    assert fa.fa_bwd_workspace_bytes(fa.FA_BF16, 1, 1, 3, 64, 0) == 2 * 256  # padded
     assert fa.fa_bwd_workspace_bytes(fa.FA_BF16, 1, 1, 3, 96, 0) == 0
     assert fa.fa_bwd_workspace_bytes(fa.FA_F32, 1, 1, 128, 64, 0) == 0
 
