@@ -179,6 +179,23 @@ __device__ inline uint32_t dma_goff(int b, int lane, int row0) {
 // Wait until this wave's direct-to-LDS loads have landed (vmcnt = 0).
 __device__ inline void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Workgroup barrier that does not wait for outstanding direct-to-LDS loads.
+// __syncthreads() is a release/acquire fence plus s_barrier, and the fence
+// makes every wave drain its vector-memory counter, i.e. wait for prefetches
+// meant to stay in flight across the barrier.  Here the wave's own LDS reads
+// are drained (lgkmcnt = 0: nothing it still reads can be overwritten by a
+// load another wave issues after the barrier) and the barrier is emitted as
+// an instruction the compiler may not move memory operations across.
+__device__ inline void barrier_keep_loads() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt untouched
+  asm volatile("s_barrier" ::: "memory");
+}
+// Barrier after this wave's loads have landed (vmcnt = lgkmcnt = 0).
+__device__ inline void barrier_after_loads() {
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // 64-bit transposing LDS read: within each 16-lane group, lane j receives
 // element j%4 of the 8-byte chunks addressed by lanes j/4, 4+j/4, 8+j/4 and
 // 12+j/4 (one element from each of four rows).

@@ -248,6 +248,215 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 }
 
+// Ping-pong variant for large grids: one workgroup = 8 waves = 256 query
+// rows, one workgroup per CU.  Waves 0-3 (group A) and 4-7 (group B) pair up
+// on the four SIMDs and run the same phase sequence one phase apart:
+//   M(j): O^T += V^T P^T for tile j-1, then S^T = K Q^T for tile j  (MFMA)
+//   X(j): mask, row max, rescale check, exp2, row sums, pack P      (VALU)
+// Every phase ends at a workgroup barrier, so while one wave of a SIMD issues
+// MFMAs the other runs its softmax: the matrix cores and the vector ALUs work
+// at the same time instead of taking turns inside one wave.  K and V tiles
+// have two LDS buffers each, filled by direct global->LDS loads issued two
+// phases before they are read (K of tile j+1 and V of tile j at phase 2j).
+constexpr int kPpBR = 256;
+
+template <typename T, int D, bool CAUSAL, int GROUP>
+__device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
+                                             const uint16_t* __restrict__ K,
+                                             const uint16_t* __restrict__ V,
+                                             uint16_t* __restrict__ O, float* __restrict__ LSE,
+                                             int N, float c, int nqt, int total, uint16_t* kb0,
+                                             uint16_t* kb1, uint16_t* vb0, uint16_t* vb1) {
+  constexpr int BC = FwdTile<D>::BC;
+  constexpr int TILE = BC * D;
+  constexpr int BLOCKS = TILE * 2 / 1024;
+  constexpr int NKB = BC / 32;
+  constexpr int NDC = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int NKC = BC / 16;
+  static_assert(BLOCKS % 8 == 0, "blocks split evenly over 8 waves");
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const int logical = xcd_logical_block(blockIdx.x, total);
+  const int bh = logical / nqt;
+  int qt = logical - bh * nqt;
+  if (CAUSAL) qt = nqt - 1 - qt;  // longest rows first
+  const int q0 = qt * kPpBR;
+  const int wq0 = q0 + wave * 32;
+  const int myq = wq0 + l32;
+
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto rQ = make_rsrc(Q + base, head_bytes);
+  const auto rK = make_rsrc(K + base, head_bytes);
+  const auto rV = make_rsrc(V + base, head_bytes);
+
+  u32x4 qf[NDC];
+#pragma unroll
+  for (int cc = 0; cc < NDC; ++cc)
+    qf[cc] = buf_load16(rQ, ((uint32_t)myq * D + 16 * cc + 8 * hh) * 2u);
+
+  // LDS offsets as in fwd16_kernel.
+  int koff[NDC];
+#pragma unroll
+  for (int cc = 0; cc < NDC; ++cc) koff[cc] = toff<D>(l32, 16 * cc + 8 * hh);
+  const int G = lane >> 4, a16 = lane & 15;
+  int voff[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      voff[db][t] = toff<D>(8 * t + 4 * (G >> 1) + (a16 >> 2), 32 * db + 16 * (G & 1) + 4 * (a16 & 3));
+
+  const int kend = CAUSAL ? min(N, q0 + kPpBR) : N;
+  const int ntiles = (kend + BC - 1) / BC;
+
+  auto dma_tile = [&](const uint16_t* dst, __amdgpu_buffer_rsrc_t r, int ts) {
+#pragma unroll
+    for (int i = 0; i < BLOCKS / 8; ++i) {
+      const int b = wave_u + 8 * i;
+      lds_dma16(r, dst + b * 512, dma_goff<D>(b, lane, ts));
+    }
+  };
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m = -INFINITY;  // reference max (log2 units), moved lazily
+  float lpart = 0.f;    // partial row sum over this lane's keys
+  f32x16 s[NKB];        // scores of the tile between its M and X phases
+  u32x4 pk[NKC];        // probabilities between X(j) and M(j+1)
+
+  auto active = [&](int j) { return !CAUSAL || j * BC <= wq0 + 31; };
+
+  auto phase_m = [&](int j, const uint16_t* Kcur, const uint16_t* Vprev) {
+    if (j >= 1 && j <= ntiles && active(j - 1)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          const uint16_t* vb = Vprev + kc * 16 * D;
+          const u32x4 a = cat(ld_lds_tr(vb + voff[db][0]), ld_lds_tr(vb + voff[db][1]));
+          oacc[db] = T::mfma(a, pk[kc], oacc[db]);
+        }
+    }
+    if (j < ntiles && active(j)) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < NDC; ++cc)
+          s[kb] = T::mfma(ld_lds16(Kcur + kb * 32 * D + koff[cc]), qf[cc], s[kb]);
+      }
+    }
+  };
+
+  auto phase_x = [&](int j) {
+    if (j < 0 || j >= ntiles || !active(j)) return;
+    const int ts = j * BC;
+    const bool need_mask = (ts + BC > N) || (CAUSAL && ts + BC - 1 > wq0);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = ts + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key >= N || (CAUSAL && key > myq)) s[kb][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    const float mt = max_halves(mx) * c;
+    if (wave_any(mt > m + kRescaleSlack)) {
+      const float mnew = fmaxf(m, mt);
+      const float alpha = fast_exp2(m - mnew);
+      m = mnew;
+      lpart *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = fast_exp2(fmaf(s[kb][8 * half + 2 * i], c, -m));
+          const float p1 = fast_exp2(fmaf(s[kb][8 * half + 2 * i + 1], c, -m));
+          rs += p0 + p1;
+          pk[2 * kb + half][i] = T::pack2(p0, p1);
+        }
+    lpart += rs;
+  };
+
+  dma_tile(kb0, rK, 0);
+  barrier_after_loads();
+  // Slots 2t .. 2t+3 cover tiles t and t+1; group B runs one slot behind.
+  constexpr bool A = GROUP == 0;
+  for (int t = 0; t <= ntiles; t += 2) {
+    if (t + 1 < ntiles) dma_tile(kb1, rK, (t + 1) * BC);
+    if (t < ntiles) dma_tile(vb0, rV, t * BC);
+    if (A) phase_m(t, kb0, vb1); else phase_x(t - 1);
+    barrier_keep_loads();
+    if (A) phase_x(t); else phase_m(t, kb0, vb1);
+    barrier_after_loads();
+    if (t + 2 < ntiles) dma_tile(kb0, rK, (t + 2) * BC);
+    if (t + 1 < ntiles) dma_tile(vb1, rV, (t + 1) * BC);
+    if (A) phase_m(t + 1, kb1, vb0); else phase_x(t);
+    barrier_keep_loads();
+    if (A) phase_x(t + 1); else phase_m(t + 1, kb1, vb0);
+    barrier_after_loads();
+  }
+
+  const float ltot = sum_halves(lpart);
+  const float inv = 1.f / ltot;
+  if (myq < N) {
+    uint16_t* Oq = O + base + (size_t)myq * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = T::pack2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+        w[1] = T::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+        st_global8(Oq + db * 32 + 8 * g + 4 * hh, w);
+      }
+    if (hh == 0) LSE[(size_t)bh * N + myq] = (m + log2f(ltot)) * kLn2;
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(512, 1)
+fwd16pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+               const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+               float* __restrict__ LSE, int N, float c, int nqt, int total) {
+  constexpr int TILE = FwdTile<D>::BC * D;
+  // Separate buffers with compile-time selection (the slot loop is unrolled
+  // over two tiles): loads into one buffer never alias reads of another.
+  __shared__ __attribute__((aligned(1024))) uint16_t kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vb1[TILE];
+  // Each group runs its own copy of the slot loop (no per-slot branch on it).
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 8) == 0)
+    fwd16pp_body<T, D, CAUSAL, 0>(Q, K, V, O, LSE, N, c, nqt, total, kb0, kb1, vb0, vb1);
+  else
+    fwd16pp_body<T, D, CAUSAL, 1>(Q, K, V, O, LSE, N, c, nqt, total, kb0, kb1, vb0, vb1);
+}
+
 // fp32 kernel: true fp32 products on the vector ALUs (no reduced-precision
 // matrix path), same online softmax.  Four lanes share one query row, each
 // holding D/4 of its q and o; a workgroup covers 64 rows and streams 32-key
@@ -336,6 +545,15 @@ fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch16(const FwdArgs& a) {
+  // Enough 256-row workgroups to give every CU at least two: ping-pong kernel.
+  const int npp = (a.N + kPpBR - 1) / kPpBR;
+  if ((long)npp * a.B * a.H >= 512) {
+    const int total = npp * a.B * a.H;
+    hipLaunchKernelGGL((fwd16pp_kernel<T, D, CAUSAL>), dim3(total), dim3(512), 0, a.stream,
+                       (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
+                       (uint16_t*)a.O, a.LSE, a.N, a.scale * kLog2e, npp, total);
+    return hipGetLastError();
+  }
   const int nqt = (a.N + kFwdBR - 1) / kFwdBR;
   const int total = nqt * a.B * a.H;
   hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,

@@ -50,6 +50,25 @@ def test_forward_small(N, causal, D, dtype):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [257, 600])
+def test_forward_many_heads(N, causal, D, dtype):
+    """Grids with at least two 256-row workgroups per CU take the ping-pong
+    forward kernel (8 waves, 256 rows); ragged N covers its tail handling."""
+    say(f"[fwd-many-heads] N={N} D={D} causal={causal} dtype={dtype}")
+    shape = (2, 256, N, D)
+    vals, devs = draw_case(300 + N, shape, dtype)
+    scale = 1.0 / np.sqrt(D)
+    o, lse = _fwd(devs, scale, causal)
+    ro, rl = oracle.attention_fwd(vals["q"], vals["k"], vals["v"], scale, causal)
+    tol = TOL[dtype]
+    eo, el = max_abs(to_f64(o), ro), max_abs(to_f64(lse), rl)
+    say(f"    max abs O={eo:.2e} LSE={el:.2e}")
+    assert eo <= tol["o"] and el <= tol["lse"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", SHAPES_N)
 def test_backward_small(N, causal, D, dtype):
     say(f"[bwd] N={N} D={D} causal={causal} dtype={dtype}")
