@@ -336,11 +336,13 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
   auto active = [&](int j) { return !CAUSAL || j * BC <= wq0 + 31; };
 
   auto phase_m = [&](int j, const uint16_t* Kcur, const uint16_t* Vprev) {
+    // Independent accumulators are interleaved (reduction step outer) so
+    // consecutive MFMAs never wait on each other's results.
     if (j >= 1 && j <= ntiles && active(j - 1)) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
+        for (int db = 0; db < NDB; ++db) {
           const uint16_t* vb = Vprev + kc * 16 * D;
           const u32x4 a = cat(ld_lds_tr(vb + voff[db][0]), ld_lds_tr(vb + voff[db][1]));
           oacc[db] = T::mfma(a, pk[kc], oacc[db]);
@@ -348,13 +350,14 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
     }
     if (j < ntiles && active(j)) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < NDC; ++cc)
+      for (int cc = 0; cc < NDC; ++cc)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
           s[kb] = T::mfma(ld_lds16(Kcur + kb * 32 * D + koff[cc]), qf[cc], s[kb]);
-      }
     }
   };
 
