@@ -37,6 +37,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -115,17 +117,17 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int bh = logical / nkt;
   const int kt = logical - bh * nkt;  // causal: small kt has the most queries, runs first
   const int k0 = kt * kDkvKeys;
-  const int wk0 = k0 + wave * 32;
+  const int wk0 = k0 + wave_u * 32;
   const int mykey = wk0 + l32;
 
   const size_t base = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto rQ = make_rsrc(Q + base, head_bytes);
-  const auto rdO = make_rsrc(dO + base, head_bytes);
+  const i32x4 rQ = rsrc_words(Q + base, head_bytes);  // direct-to-LDS sources
+  const i32x4 rdO = rsrc_words(dO + base, head_bytes);
+  const i32x4 rL = rsrc_words(lse2 + (size_t)bh * N, (uint32_t)N * 4);
+  const i32x4 rD = rsrc_words(delta + (size_t)bh * N, (uint32_t)N * 4);
   const auto rK = make_rsrc(K + base, head_bytes);
   const auto rV = make_rsrc(V + base, head_bytes);
-  const auto rL = make_rsrc(lse2 + (size_t)bh * N, (uint32_t)N * 4);
-  const auto rD = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
 
   // B operands of S = Q K^T and dP = dO V^T: lane holds row `mykey` of K, V.
   u32x4 kf[NDC], vf[NDC];
@@ -165,11 +167,9 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       lds_dma16(rdO, S0 + TILE + b * 512, goff);
     }
     if (wave_u == 0)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, to_lds(S0 + 2 * TILE), 4,
-                                               (uint32_t)(qs + lane) * 4u, 0, 0, 0);
+      lds_dma4(rL, S0 + 2 * TILE, (uint32_t)(qs + lane) * 4u);
     else if (wave_u == 1)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, to_lds(S0 + 2 * TILE + 128), 4,
-                                               (uint32_t)(qs + lane) * 4u, 0, 0, 0);
+      lds_dma4(rD, S0 + 2 * TILE + 128, (uint32_t)(qs + lane) * 4u);
   };
 
   f32x16 dkacc[NDB], dvacc[NDB];
@@ -181,29 +181,42 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       dvacc[db][r] = 0.f;
     }
 
-  auto tile = [&](const uint16_t* S0, int qs) {
+  // One query tile.  MASKED: the tile overlaps this workgroup's keys on the
+  // causal diagonal (per-wave skip of blocks wholly above it, element mask
+  // on the rest); otherwise every (query, key) pair is visible and the body
+  // is straight-line code, so the scheduler can overlap one block's softmax
+  // arithmetic with the other block's MFMAs.
+  auto tile = [&](const uint16_t* S0, int qs, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
+    constexpr int NQB = BR / 32;
     const uint16_t* Qs = S0;
     const uint16_t* dOs = S0 + TILE;
     const float* lse2s = reinterpret_cast<const float*>(S0 + 2 * TILE);
     const float* dlts = lse2s + 64;
+    // block qb holds queries that see some key of this wave
+    auto live = [&](int qb) { return !MASKED || qs + qb * 32 + 31 >= wk0; };
+    f32x16 s[NQB], dp[NQB];
 #pragma unroll
-    for (int qb = 0; qb < BR / 32; ++qb) {
-      const int qb0 = qs + qb * 32;
-      if (CAUSAL && qb0 + 31 < wk0) continue;  // every query precedes every key
-      f32x16 s, dp;
+    for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
+        s[qb][r] = 0.f;
+        dp[qb][r] = 0.f;
       }
 #pragma unroll
-      for (int cc = 0; cc < NDC; ++cc) {
-        s = T::mfma(ld_lds16(Qs + qb * 32 * D + roff[cc]), kf[cc], s);
-        dp = T::mfma(ld_lds16(dOs + qb * 32 * D + roff[cc]), vf[cc], dp);
-      }
-      // lane: key `mykey`; register r: query qb0 + 8*(r/4) + 4*hh + r%4
-      const bool need_mask = CAUSAL && qb0 < wk0 + 31;
-      u32x4 pp[2], dsp[2];
+    for (int cc = 0; cc < NDC; ++cc)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+        if (live(qb)) {
+          s[qb] = T::mfma(ld_lds16(Qs + qb * 32 * D + roff[cc]), kf[cc], s[qb]);
+          dp[qb] = T::mfma(ld_lds16(dOs + qb * 32 * D + roff[cc]), vf[cc], dp[qb]);
+        }
+    // lane: key `mykey`; register r of block qb: query
+    // qs + 32qb + 8*(r/4) + 4*hh + r%4
+    u32x4 pp[NQB][2], dsp[NQB][2];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const bool need_mask = MASKED && qs + qb * 32 < wk0 + 31;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int qo = qb * 32 + 8 * g + 4 * hh;
@@ -213,42 +226,57 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          float pv = fast_exp2(fmaf(s[r], c, -l4[e]));
+          float pv = fast_exp2(fmaf(s[qb][r], c, -l4[e]));
           if (need_mask && qs + qo + e < mykey) pv = 0.f;
           p[e] = pv;
-          ds[e] = pv * (dp[r] - d4[e]);
+          ds[e] = pv * (dp[qb][r] - d4[e]);
         }
-        pp[g >> 1][2 * (g & 1)] = T::pack2(p[0], p[1]);
-        pp[g >> 1][2 * (g & 1) + 1] = T::pack2(p[2], p[3]);
-        dsp[g >> 1][2 * (g & 1)] = T::pack2(ds[0], ds[1]);
-        dsp[g >> 1][2 * (g & 1) + 1] = T::pack2(ds[2], ds[3]);
+        pp[qb][g >> 1][2 * (g & 1)] = T::pack2(p[0], p[1]);
+        pp[qb][g >> 1][2 * (g & 1) + 1] = T::pack2(p[2], p[3]);
+        dsp[qb][g >> 1][2 * (g & 1)] = T::pack2(ds[0], ds[1]);
+        dsp[qb][g >> 1][2 * (g & 1) + 1] = T::pack2(ds[2], ds[3]);
       }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int qc = 0; qc < 2; ++qc) {
-          const int rb = (qb * 32 + qc * 16) * D;
-          const u32x4 ag =
-              cat(ld_lds_tr(dOs + rb + toffs[db][0]), ld_lds_tr(dOs + rb + toffs[db][1]));
-          dvacc[db] = T::mfma(ag, pp[qc], dvacc[db]);
-          const u32x4 aq =
-              cat(ld_lds_tr(Qs + rb + toffs[db][0]), ld_lds_tr(Qs + rb + toffs[db][1]));
-          dkacc[db] = T::mfma(aq, dsp[qc], dkacc[db]);
-        }
     }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+      if (live(qb)) {
+#pragma unroll
+        for (int qc = 0; qc < 2; ++qc)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const int rb = (qb * 32 + qc * 16) * D;
+            const u32x4 ag =
+                cat(ld_lds_tr(dOs + rb + toffs[db][0]), ld_lds_tr(dOs + rb + toffs[db][1]));
+            dvacc[db] = T::mfma(ag, pp[qb][qc], dvacc[db]);
+            const u32x4 aq =
+                cat(ld_lds_tr(Qs + rb + toffs[db][0]), ld_lds_tr(Qs + rb + toffs[db][1]));
+            dkacc[db] = T::mfma(aq, dsp[qb][qc], dkacc[db]);
+          }
+      }
   };
-
-  if (ntiles > 0) dma(smem0, qstart);
+  // Causal: the first tiles (queries k0 .. k0+127) straddle the diagonal of
+  // this workgroup's keys and take the masked body, unpipelined; every later
+  // tile is wholly visible and runs the straight-line body, double-buffered.
+  int t = 0;
+  const int ndiag = CAUSAL ? min(ntiles, kDkvKeys / BR) : 0;
+  for (; t < ndiag; ++t) {
+    dma(smem0, qstart + t * BR);
+    wait_dma();
+    __syncthreads();
+    tile(smem0, qstart + t * BR, std::true_type());
+    __syncthreads();
+  }
+  if (t < ntiles) dma(smem0, qstart + t * BR);
   wait_dma();
   __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
+  for (; t < ntiles; t += 2) {
     if (t + 1 < ntiles) dma(smem1, qstart + (t + 1) * BR);
-    tile(smem0, qstart + t * BR);
+    tile(smem0, qstart + t * BR, std::false_type());
     wait_dma();
     __syncthreads();
     if (t + 1 >= ntiles) break;
     if (t + 2 < ntiles) dma(smem0, qstart + (t + 2) * BR);
-    tile(smem1, qstart + (t + 1) * BR);
+    tile(smem1, qstart + (t + 1) * BR, std::false_type());
     wait_dma();
     __syncthreads();
   }
@@ -322,8 +350,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const auto rQ = make_rsrc(Q + base, head_bytes);
   const auto rdO = make_rsrc(dO + base, head_bytes);
-  const auto rK = make_rsrc(K + base, head_bytes);
-  const auto rV = make_rsrc(V + base, head_bytes);
+  const i32x4 rK = rsrc_words(K + base, head_bytes);  // direct-to-LDS sources
+  const i32x4 rV = rsrc_words(V + base, head_bytes);
 
   u32x4 qf[NDC], gf[NDC];
 #pragma unroll
@@ -367,67 +395,88 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  auto tile = [&](const uint16_t* S0, int ts) {
+  // One key tile.  MASKED: a ragged tail or a tile on the causal diagonal of
+  // this workgroup's rows (per-wave skip, element mask); otherwise the body
+  // is straight-line code.
+  auto tile = [&](const uint16_t* S0, int ts, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const uint16_t* Ks = S0;
     const uint16_t* Vs = S0 + TILE;
-    if (!CAUSAL || ts <= wq0 + 31) {
-      const bool need_mask = (ts + BC > N) || (CAUSAL && ts + BC - 1 > wq0);
-      u32x4 dsk[NKC];
+    if (MASKED && CAUSAL && ts > wq0 + 31) return;  // no key visible to this wave
+    const bool need_mask = MASKED && ((ts + BC > N) || (CAUSAL && ts + BC - 1 > wq0));
+    f32x16 s[NKB], dp[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        f32x16 s, dp;
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[r] = 0.f;
-          dp[r] = 0.f;
-        }
-#pragma unroll
-        for (int cc = 0; cc < NDC; ++cc) {
-          s = T::mfma(ld_lds16(Ks + kb * 32 * D + roff[cc]), qf[cc], s);
-          dp = T::mfma(ld_lds16(Vs + kb * 32 * D + roff[cc]), gf[cc], dp);
-        }
-        // lane: query `myq`; register r: key ts + kb*32 + 8*(r/4) + 4*hh + r%4
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float ds2[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int r = 8 * half + 2 * i + e;
-              float pv = fast_exp2(fmaf(s[r], c, -lse2));
-              if (need_mask) {
-                const int key = ts + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                if (key >= N || (CAUSAL && key > myq)) pv = 0.f;
-              }
-              ds2[e] = pv * (dp[r] - dlt);
-            }
-            dsk[2 * kb + half][i] = T::pack2(ds2[0], ds2[1]);
-          }
+      for (int r = 0; r < 16; ++r) {
+        s[kb][r] = 0.f;
+        dp[kb][r] = 0.f;
       }
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+    for (int cc = 0; cc < NDC; ++cc)
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-          const uint16_t* kb16 = Ks + kc * 16 * D;
-          const u32x4 a = cat(ld_lds_tr(kb16 + toffs[db][0]), ld_lds_tr(kb16 + toffs[db][1]));
-          acc[db] = T::mfma(a, dsk[kc], acc[db]);
+      for (int kb = 0; kb < NKB; ++kb) {
+        s[kb] = T::mfma(ld_lds16(Ks + kb * 32 * D + roff[cc]), qf[cc], s[kb]);
+        dp[kb] = T::mfma(ld_lds16(Vs + kb * 32 * D + roff[cc]), gf[cc], dp[kb]);
+      }
+    // lane: query `myq`; register r of block kb: key ts + kb*32 + 8*(r/4) + 4*hh + r%4
+    u32x4 dsk[NKC];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float ds2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 8 * half + 2 * i + e;
+            float pv = fast_exp2(fmaf(s[kb][r], c, -lse2));
+            if (need_mask) {
+              const int key = ts + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+              if (key >= N || (CAUSAL && key > myq)) pv = 0.f;
+            }
+            ds2[e] = pv * (dp[kb][r] - dlt);
+          }
+          dsk[2 * kb + half][i] = T::pack2(ds2[0], ds2[1]);
         }
-    }
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const uint16_t* kb16 = Ks + kc * 16 * D;
+        const u32x4 a = cat(ld_lds_tr(kb16 + toffs[db][0]), ld_lds_tr(kb16 + toffs[db][1]));
+        acc[db] = T::mfma(a, dsk[kc], acc[db]);
+      }
   };
 
-  dma(smem0, 0);
+  // Tiles wholly visible to every row of the workgroup (no tail, not past
+  // the causal diagonal) run the straight-line body, double-buffered; the
+  // remaining ones (at the end) the masked body, unpipelined.
+  const int nfull = min(N / BC, CAUSAL ? (q0 + 1) / BC : ntiles);
+  int t = 0;
+  if (nfull > 0) dma(smem0, 0);
   wait_dma();
   __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
-    if (t + 1 < ntiles) dma(smem1, (t + 1) * BC);
-    tile(smem0, t * BC);
+  for (; t < nfull; t += 2) {
+    if (t + 1 < nfull) dma(smem1, (t + 1) * BC);
+    tile(smem0, t * BC, std::false_type());
     wait_dma();
     __syncthreads();
-    if (t + 1 >= ntiles) break;
-    if (t + 2 < ntiles) dma(smem0, (t + 2) * BC);
-    tile(smem1, (t + 1) * BC);
+    if (t + 1 >= nfull) {
+      t += 1;
+      break;
+    }
+    if (t + 2 < nfull) dma(smem0, (t + 2) * BC);
+    tile(smem1, (t + 1) * BC, std::false_type());
     wait_dma();
+    __syncthreads();
+  }
+  for (; t < ntiles; ++t) {
+    dma(smem0, t * BC);
+    wait_dma();
+    __syncthreads();
+    tile(smem0, t * BC, std::true_type());
     __syncthreads();
   }
 

@@ -158,12 +158,39 @@ __device__ inline lds_void* to_lds(const void* p) {
   return (lds_void*)((__attribute__((address_space(3))) char*)(p));
 }
 
+// Buffer resource as four dwords (for inline assembly): 48-bit base, stride
+// 0, `bytes` records, gfx9 dword format.  Loads past `bytes` return zeros.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ inline i32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const unsigned long long p = (unsigned long long)base;
+  return i32x4{(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
 // One 1 KiB block of a swizzled tile straight from global memory into LDS:
-// lane l fetches 16 bytes at byte offset `goff` of the buffer `r` and the
-// hardware writes them to lds_block + 16*l (lds_block is wave-uniform).
-// Offsets past the buffer's end write zeros.
-__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, const uint16_t* lds_block, uint32_t goff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(lds_block), 16, goff, 0, 0, 0);
+// lane l fetches 16 bytes at byte offset `goff` of the buffer and the
+// hardware writes them to lds_block + 16*l (lds_block is wave-uniform, passed
+// in M0).  Offsets past the buffer's end write zeros.  Written as inline
+// assembly so that the compiler does not track these LDS writes itself: it
+// would otherwise make LDS reads of *other* buffers wait for every load in
+// flight.  The kernels order them explicitly (vmcnt waits before the
+// barriers that publish a buffer); the "memory" clobber keeps other memory
+// accesses from moving across.  M0 is only used this way in these kernels.
+__device__ inline void lds_dma16(const i32x4& r, const uint16_t* lds_block, uint32_t goff) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(
+      (__attribute__((address_space(3))) const uint16_t*)lds_block);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(goff), "s"(r)
+               : "memory");
+}
+// Same for 4-byte elements (64 lanes x 4 bytes = 256 bytes).
+__device__ inline void lds_dma4(const i32x4& r, const void* lds_block, uint32_t goff) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(
+      (__attribute__((address_space(3))) const char*)lds_block);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(goff), "s"(r)
+               : "memory");
 }
 
 // Global byte offset lane `lane` must fetch for 1 KiB block `b` of a tile

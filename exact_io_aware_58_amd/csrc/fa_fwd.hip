@@ -37,6 +37,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -93,8 +95,8 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const size_t base = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const auto rQ = make_rsrc(Q + base, head_bytes);
-  const auto rK = make_rsrc(K + base, head_bytes);
-  const auto rV = make_rsrc(V + base, head_bytes);
+  const i32x4 rK = rsrc_words(K + base, head_bytes);  // direct-to-LDS sources
+  const i32x4 rV = rsrc_words(V + base, head_bytes);
 
   // B operand of S^T = K Q^T: lane (l32, hh) holds Q[myq][16c + 8hh .. +7]
   // (zeros past the last row).
@@ -147,20 +149,24 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   float m = -INFINITY;
   float lpart = 0.f;
 
-  auto tile = [&](const uint16_t* Ks, int ts) {
+  // MASKED: ragged tail or causal-diagonal tile (per-wave skip, element
+  // mask); the others run straight-line code.
+  auto tile = [&](const uint16_t* Ks, int ts, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const uint16_t* Vs = Ks + TILE;
-    if (!CAUSAL || ts <= wq0 + 31) {
+    if (!MASKED || !CAUSAL || ts <= wq0 + 31) {
       // S^T[key][q] for the wave's 32 queries and the tile's BC keys.
       f32x16 s[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < NDC; ++cc)
+      for (int cc = 0; cc < NDC; ++cc)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
           s[kb] = T::mfma(ld_lds16(Ks + kb * 32 * D + koff[cc]), qf[cc], s[kb]);
-      }
-      const bool need_mask = (ts + BC > N) || (CAUSAL && ts + BC - 1 > wq0);
+      const bool need_mask = MASKED && ((ts + BC > N) || (CAUSAL && ts + BC - 1 > wq0));
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -204,9 +210,9 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           }
       lpart += rs;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
+        for (int db = 0; db < NDB; ++db) {
           const uint16_t* vb = Vs + kc * 16 * D;
           const u32x4 a = cat(ld_lds_tr(vb + voff[db][0]), ld_lds_tr(vb + voff[db][1]));
           oacc[db] = T::mfma(a, pk[kc], oacc[db]);
@@ -214,19 +220,33 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   };
 
-  dma(smem0, 0);
+  // Tiles visible to every row (no tail, not past the causal diagonal):
+  // straight-line body, double-buffered; the rest (at the end): masked body.
+  const int nfull = min(N / BC, CAUSAL ? (q0 + 1) / BC : ntiles);
+  int t = 0;
+  if (nfull > 0) dma(smem0, 0);
   wait_dma();
   __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
+  for (; t < nfull; t += 2) {
     // even tile in stage 0 while the odd one lands in stage 1, then swap
-    if (t + 1 < ntiles) dma(smem1, (t + 1) * BC);
-    tile(smem0, t * BC);
+    if (t + 1 < nfull) dma(smem1, (t + 1) * BC);
+    tile(smem0, t * BC, std::false_type());
     wait_dma();
     __syncthreads();
-    if (t + 1 >= ntiles) break;
-    if (t + 2 < ntiles) dma(smem0, (t + 2) * BC);
-    tile(smem1, (t + 1) * BC);
+    if (t + 1 >= nfull) {
+      t += 1;
+      break;
+    }
+    if (t + 2 < nfull) dma(smem0, (t + 2) * BC);
+    tile(smem1, (t + 1) * BC, std::false_type());
     wait_dma();
+    __syncthreads();
+  }
+  for (; t < ntiles; ++t) {
+    dma(smem0, t * BC);
+    wait_dma();
+    __syncthreads();
+    tile(smem0, t * BC, std::true_type());
     __syncthreads();
   }
 
@@ -292,8 +312,8 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
   const size_t base = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const auto rQ = make_rsrc(Q + base, head_bytes);
-  const auto rK = make_rsrc(K + base, head_bytes);
-  const auto rV = make_rsrc(V + base, head_bytes);
+  const i32x4 rK = rsrc_words(K + base, head_bytes);  // direct-to-LDS sources
+  const i32x4 rV = rsrc_words(V + base, head_bytes);
 
   u32x4 qf[NDC];
 #pragma unroll
@@ -315,7 +335,7 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
   const int kend = CAUSAL ? min(N, q0 + kPpBR) : N;
   const int ntiles = (kend + BC - 1) / BC;
 
-  auto dma_tile = [&](const uint16_t* dst, __amdgpu_buffer_rsrc_t r, int ts) {
+  auto dma_tile = [&](const uint16_t* dst, const i32x4& r, int ts) {
 #pragma unroll
     for (int i = 0; i < BLOCKS / 8; ++i) {
       const int b = wave_u + 8 * i;
@@ -405,10 +425,12 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
     lpart += rs;
   };
 
+  // K of tile j+1 and V of tile j are loaded at slot 2j (two buffers each)
+  // and first read at slot 2j+2; the odd slots' barriers wait for them.
   dma_tile(kb0, rK, 0);
   barrier_after_loads();
-  // Slots 2t .. 2t+3 cover tiles t and t+1; group B runs one slot behind.
   constexpr bool A = GROUP == 0;
+  // Slots 2t .. 2t+3 cover tiles t and t+1; group B runs one slot behind.
   for (int t = 0; t <= ntiles; t += 2) {
     if (t + 1 < ntiles) dma_tile(kb1, rK, (t + 1) * BC);
     if (t < ntiles) dma_tile(vb0, rV, t * BC);
