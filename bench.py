@@ -194,6 +194,74 @@ def cpu_baseline(w, rows):
     }
 
 
+def run_sweep(ns, heads=16, D=64, reps=5):
+    """Sequence-length sweep (one JSON line per N): forward and backward time
+    and device memory of this library beside the three-kernel PyTorch path
+    (matmul, softmax, matmul on the same GPU, bf16, non-causal), which
+    materialises the N x N scores and probabilities in HBM.  The reference
+    path runs forward only (its autograd backward issues batched bf16
+    products on transposed views, which are not run on this GPU)."""
+    import numpy as np
+    import torch
+    from exact_io_aware_58_amd import fa, inputs
+
+    scale = 1.0 / D ** 0.5
+    for N in ns:
+        w = inputs.Workload(f"sweep_n{N}", 7, 1, heads, N, D, "bf16", False, True)
+        devs = {n: upload(raw, "bf16") for n, (_, raw) in inputs.make_inputs(w).items()}
+        q, k, v, do = devs["q"], devs["k"], devs["v"], devs["do"]
+        f, b = flops(w)
+        row = {"N": N, "B": 1, "H": heads, "D": D, "causal": False}
+
+        def timed(fn):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        o, lse = fa.forward(q, k, v, scale, False)
+        dq, dk, dv = fa.backward(q, k, v, o, do, lse, scale, False)
+        torch.cuda.synchronize()
+        row["fa_extra_bytes"] = torch.cuda.max_memory_allocated() - base
+        ws = torch.empty(fa.workspace_bytes(q), dtype=torch.uint8, device=q.device)
+        row["fa_fwd_ms"] = timed(lambda: fa.forward(q, k, v, scale, False, out=o, lse=lse))
+        row["fa_bwd_ms"] = timed(lambda: fa.backward(q, k, v, o, do, lse, scale, False, dq=dq,
+                                                     dk=dk, dv=dv, workspace=ws))
+        row["fa_fwd_tflops"] = f / row["fa_fwd_ms"] / 1e9
+        row["fa_bwd_tflops"] = b / row["fa_bwd_ms"] / 1e9
+        del dq, dk, dv, ws
+
+        def naive():
+            s_ = torch.matmul(q, k.transpose(-2, -1).contiguous()) * scale
+            p_ = torch.softmax(s_, dim=-1)
+            return torch.matmul(p_, v)
+
+        try:
+            torch.cuda.synchronize()
+            base = torch.cuda.memory_allocated()
+            torch.cuda.reset_peak_memory_stats()
+            ref = naive()
+            torch.cuda.synchronize()
+            row["naive_extra_bytes"] = torch.cuda.max_memory_allocated() - base
+            row["naive_max_abs_diff"] = float((ref.float() - o.float()).abs().max())
+            del ref
+            row["naive_fwd_ms"] = timed(naive)
+            row["fwd_speedup"] = row["naive_fwd_ms"] / row["fa_fwd_ms"]
+        except torch.cuda.OutOfMemoryError:
+            row["naive_fwd_ms"] = "out of memory"
+        torch.cuda.empty_cache()
+        print(json.dumps(row), flush=True)
+        del q, k, v, do, o, lse, devs
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,7 +275,13 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size kernel for scaling HBM byte counters)")
+    ap.add_argument("--sweep", default="",
+                    help="comma-separated sequence lengths: print one JSON line per N "
+                         "comparing with the three-kernel PyTorch path instead of the bench line")
     args = ap.parse_args()
+    if args.sweep:
+        run_sweep([int(x) for x in args.sweep.split(",")])
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the attention path is built and timed on a single MI355X)", file=sys.stderr)

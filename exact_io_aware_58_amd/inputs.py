@@ -54,6 +54,9 @@ WORKLOADS = {
                    input_mult=0.5, check_rows=256),
     "c5": Workload("train_causal_bf16_b1h16n65536d64", 5, 1, 16, 65536, 64, "bf16", True, True,
                    check_rows=128),
+    # Scale test of the linear-memory claim: a 128K-token causal training step.
+    "n128k": Workload("train_causal_bf16_b1h8n131072d64", 6, 1, 8, 131072, 64, "bf16", True, True,
+                      check_rows=64),
 }
 
 

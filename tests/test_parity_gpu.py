@@ -236,3 +236,38 @@ def test_workload_c5_long_causal_training_subset():
     say(f"    {len(krows)} key rows: dK={ek:.2e} dV={ev:.2e}")
     assert eo <= 2e-2 and el <= 1e-3 and eq <= 5e-2
     assert ek <= 5e-2 and ev <= 5e-2
+
+
+def test_workload_n128k_causal_training_subset():
+    """A 131072-token causal forward + backward on one GPU (device memory
+    stays linear in N: the library allocates nothing), checked on seeded
+    query rows (O, LSE, dQ) and key rows of head 0 (dK, dV)."""
+    w = inputs.WORKLOADS["n128k"]
+    say(f"[{w.name}]")
+    vals, devs = _workload_devs(w)
+    before = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    o, lse = _fwd(devs, w.scale, True)
+    dq, dk, dv = fa.backward(devs["q"], devs["k"], devs["v"], o, devs["do"], lse, w.scale, True)
+    torch.cuda.synchronize()
+    peak_extra = torch.cuda.max_memory_allocated() - before
+    # outputs (O, dQ, dK, dV, LSE) and the workspace; nothing of size N x N
+    assert peak_extra <= 4 * o.numel() * 2 + 3 * lse.numel() * 4 + (1 << 22)
+    qrows = inputs.check_row_subset(w)
+    ro, rl = oracle.attention_fwd_rows(vals["q"], vals["k"], vals["v"], w.scale, True, qrows)
+    rq = oracle.attention_bwd_query_rows(vals["q"], vals["k"], vals["v"], vals["do"], w.scale,
+                                         True, qrows)
+    eo = max_abs(_sampled(o, qrows), ro)
+    el = max_abs(to_f64(lse)[tuple(qrows.T)], rl)
+    eq = rel_to_max(_sampled(dq, qrows), rq)
+    say(f"    {len(qrows)} query rows: O={eo:.2e} LSE={el:.2e} dQ={eq:.2e}")
+    krows = np.array([r for r in _key_rows_two_heads(w, count=48) if r[1] == 0][:32], dtype=np.int64)
+    say("    oracle row statistics of head 0 ...")
+    stats = {(0, 0): oracle.row_stats(vals["q"], vals["k"], vals["v"], vals["do"], w.scale, True,
+                                      0, 0, block_rows=1024)}
+    rk, rv = oracle.attention_bwd_key_rows(vals["q"], vals["k"], vals["v"], vals["do"], w.scale,
+                                           True, krows, stats=stats)
+    ek, ev = rel_to_max(_sampled(dk, krows), rk), rel_to_max(_sampled(dv, krows), rv)
+    say(f"    {len(krows)} key rows: dK={ek:.2e} dV={ev:.2e}")
+    assert eo <= 2e-2 and el <= 1e-3 and eq <= 5e-2
+    assert ek <= 5e-2 and ev <= 5e-2
