@@ -4,6 +4,8 @@ from .attention import (  # noqa: F401
     attention_bwd_key_rows,
     attention_bwd_query_rows,
     attention_fwd,
+    attention_fwd_partial,
     attention_fwd_rows,
+    merge_partials,
     row_stats,
 )

@@ -40,6 +40,15 @@ Large N.  S is materialised one block of query rows at a time; each block
 still sees every key of its rows, so this is the exact two-pass softmax per
 row, not an online rescaling.
 
+Partial attention and merging (the building block of sequence-parallel /
+ring attention, not on the pages): a block of Nq queries at global positions
+q_pos + i attends to a block of Nk keys at positions k_pos + j, the causal
+mask keeping key j iff k_pos + j <= q_pos + i.  A row that sees no key has
+O = 0 and LSE = -inf.  Two partial results of the same queries over disjoint
+key sets combine exactly as the online softmax combines tiles ([guanweilu]
+"FlashAttention 的三板斧", second technique, applied to whole blocks):
+LSE = ln(e^LSE_a + e^LSE_b), O = e^(LSE_a - LSE) O_a + e^(LSE_b - LSE) O_b.
+
 Parity pins (tests/test_oracle.py): closed forms (Q=0, one-hot keys, constant
 V, N=1, scale=0, two-key log-sum-exp), invariants (joint key/value
 permutation, query permutation, key shift), pure-Python brute force on tiny
@@ -52,6 +61,8 @@ import numpy as np
 
 __all__ = [
     "attention_fwd",
+    "attention_fwd_partial",
+    "merge_partials",
     "attention_bwd",
     "attention_fwd_rows",
     "attention_bwd_query_rows",
@@ -226,3 +237,50 @@ def attention_bwd_key_rows(q, k, v, do, scale, causal, rows, block_rows=_DEFAULT
         dv[n] = p @ g2
         dk[n] = scale * (ds @ q2)
     return dk, dv
+
+
+def attention_fwd_partial(q, k, v, scale, causal, q_pos=0, k_pos=0):
+    """(O, LSE) of queries q (B, H, Nq, D) against keys/values k, v
+    (B, H, Nk, D) whose rows sit at global positions q_pos + i and k_pos + j.
+    Causal: key j is visible to query i iff k_pos + j <= q_pos + i.  Rows
+    with no visible key get O = 0 and LSE = -inf."""
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] \
+            or q.shape[3] != k.shape[3]:
+        raise ValueError("Q (B,H,Nq,D), K and V (B,H,Nk,D) expected")
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    o = np.zeros((B, H, Nq, D))
+    lse = np.full((B, H, Nq), -np.inf)
+    qpos = q_pos + np.arange(Nq)[:, None]
+    kpos = k_pos + np.arange(Nk)[None, :]
+    visible = (kpos <= qpos) if causal else np.ones((Nq, Nk), dtype=bool)
+    rows = visible.any(axis=1)
+    for b in range(B):
+        for h in range(H):
+            s = scale * (q[b, h] @ k[b, h].T)
+            s = np.where(visible, s, -np.inf)[rows]
+            if s.shape[0] == 0:
+                continue
+            p, l = _softmax_rows(s)
+            o[b, h, rows] = p @ v[b, h]
+            lse[b, h, rows] = l
+    return o, lse
+
+
+def merge_partials(o_a, lse_a, o_b, lse_b):
+    """Combine two partial results of the same query rows over disjoint key
+    sets: LSE = ln(e^LSE_a + e^LSE_b), O = e^(LSE_a-LSE) O_a + e^(LSE_b-LSE) O_b.
+    Rows empty in both stay O = 0, LSE = -inf."""
+    o_a, o_b = _as64(o_a), _as64(o_b)
+    lse_a, lse_b = _as64(lse_a), _as64(lse_b)
+    m = np.maximum(lse_a, lse_b)
+    finite = np.isfinite(m)
+    ms = np.where(finite, m, 0.0)
+    wa = np.where(finite, np.exp(lse_a - ms), 0.0)
+    wb = np.where(finite, np.exp(lse_b - ms), 0.0)
+    tot = wa + wb
+    lse = np.where(finite, ms + np.log(np.where(finite, tot, 1.0)), -np.inf)
+    denom = np.where(finite, tot, 1.0)[..., None]
+    o = (wa[..., None] * o_a + wb[..., None] * o_b) / denom
+    return o, lse

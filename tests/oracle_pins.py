@@ -254,13 +254,19 @@ def pin_causal_first_row(fwd, bwd):
 
 # ---------------------------------------------------------------- brute force
 
-def _brute(q, k, v, scale, causal):
-    """Pure-Python scalar attention: explicit loops, math.exp, no numpy."""
+def _brute(q, k, v, scale, causal, q_pos=0, k_pos=0):
+    """Pure-Python scalar attention: explicit loops, math.exp, no numpy.
+    Query i sits at position q_pos + i, key j at k_pos + j; a row with no
+    visible key gets O = 0, LSE = -inf."""
     B, H, N, D = q.shape
+    Nk = k.shape[2]
     out = [[[[0.0] * D for _ in range(N)] for _ in range(H)] for _ in range(B)]
     lse = [[[0.0] * N for _ in range(H)] for _ in range(B)]
     for b, h, i in itertools.product(range(B), range(H), range(N)):
-        keys = range(i + 1) if causal else range(N)
+        keys = [j for j in range(Nk) if not causal or k_pos + j <= q_pos + i]
+        if not keys:
+            lse[b][h][i] = -math.inf
+            continue
         s = {}
         for j in keys:
             acc = 0.0
@@ -356,3 +362,87 @@ BACKWARD_PINS = [
     pin_torch_sdpa,
 ]
 ALL_PINS = FORWARD_PINS + BACKWARD_PINS
+
+
+# ---------------------------------------------------------------- partial + merge
+# These take part(q, k, v, scale, causal, q_pos, k_pos) -> (O, LSE) and
+# merge(o_a, lse_a, o_b, lse_b) -> (O, LSE).
+
+def _close_lse(a, b, what):
+    a, b = np.asarray(a), np.asarray(b)
+    assert np.array_equal(np.isneginf(a), np.isneginf(b)), f"{what}: empty rows differ"
+    fin = np.isfinite(b)
+    _close(a[fin], b[fin], what=what)
+
+
+def pin_partial_brute_force(part, merge):
+    """Rectangular blocks at offset positions (including rows that see no key
+    and blocks wholly visible) against scalar loops."""
+    rng = np.random.default_rng(61)
+    for Nq, Nk, q_pos, k_pos in ((5, 7, 10, 8), (4, 6, 0, 3), (6, 3, 0, 0), (3, 5, 20, 0),
+                                 (4, 4, 0, 9)):
+        q = rng.standard_normal((1, 2, Nq, 3))
+        k, v = rng.standard_normal((1, 2, Nk, 3)), rng.standard_normal((1, 2, Nk, 3))
+        for causal in (False, True):
+            o, lse = part(q, k, v, 0.9, causal, q_pos, k_pos)
+            bo, bl = _brute(q, k, v, 0.9, causal, q_pos, k_pos)
+            _close(o, bo, what=f"partial O {Nq, Nk, q_pos, k_pos} c={causal}")
+            _close_lse(lse, bl, what=f"partial LSE {Nq, Nk, q_pos, k_pos} c={causal}")
+
+
+def pin_partial_empty_rows(part, merge):
+    """Queries placed before every key see nothing under the causal mask."""
+    rng = np.random.default_rng(62)
+    q, k, v = (rng.standard_normal((1, 1, 4, 2)) for _ in range(3))
+    o, lse = part(q, k, v, 1.0, True, 0, 100)
+    _close(o, np.zeros_like(o), what="empty rows O")
+    assert np.all(np.isneginf(lse)), "empty rows LSE"
+
+
+def pin_merge_of_key_blocks_is_full_attention(part, merge):
+    """Splitting the keys into blocks, attending to each block and merging the
+    partial results gives plain attention over all keys (the online softmax
+    applied to whole blocks)."""
+    rng = np.random.default_rng(63)
+    N, D = 11, 4
+    q, k, v = (rng.standard_normal((2, 2, N, D)) for _ in range(3))
+    for causal in (False, True):
+        for cuts in ((5,), (3, 7), (1, 2, 10)):
+            edges = [0, *cuts, N]
+            o, lse = None, None
+            for a, b in zip(edges[:-1], edges[1:]):
+                po, pl = part(q, k[:, :, a:b], v[:, :, a:b], 0.7, causal, 0, a)
+                o, lse = (po, pl) if o is None else merge(o, lse, po, pl)
+            bo, bl = _brute(q, k, v, 0.7, causal)
+            _close(o, bo, atol=1e-12, what=f"merged blocks O {cuts} c={causal}")
+            _close(lse, bl, atol=1e-12, what=f"merged blocks LSE {cuts} c={causal}")
+
+
+def pin_merge_identities(part, merge):
+    """An empty partial is the identity; merging is symmetric; two single-key
+    partials merge to the two-key softmax (sigmoid weights)."""
+    rng = np.random.default_rng(64)
+    o1, o2 = rng.standard_normal((1, 1, 3, 2)), rng.standard_normal((1, 1, 3, 2))
+    l1, l2 = rng.standard_normal((1, 1, 3)), rng.standard_normal((1, 1, 3))
+    empty_o, empty_l = np.zeros_like(o1), np.full_like(l1, -np.inf)
+    mo, ml = merge(o1, l1, empty_o, empty_l)
+    _close(mo, o1, what="merge with empty O")
+    _close(ml, l1, what="merge with empty LSE")
+    mo, ml = merge(empty_o, empty_l, empty_o, empty_l)
+    _close(mo, empty_o, what="merge of empties O")
+    assert np.all(np.isneginf(ml)), "merge of empties LSE"
+    a_o, a_l = merge(o1, l1, o2, l2)
+    b_o, b_l = merge(o2, l2, o1, l1)
+    _close(a_o, b_o, what="merge symmetric O")
+    _close(a_l, b_l, what="merge symmetric LSE")
+    w = 1.0 / (1.0 + np.exp(l2 - l1))
+    _close(a_o, w[..., None] * o1 + (1 - w)[..., None] * o2, what="merge sigmoid weights")
+    _close(a_l, np.maximum(l1, l2) + np.log1p(np.exp(-np.abs(l1 - l2))), what="merge log-sum-exp")
+
+
+PARTIAL_PINS = [
+    pin_partial_brute_force,
+    pin_partial_empty_rows,
+    pin_merge_of_key_blocks_is_full_attention,
+    pin_merge_identities,
+]

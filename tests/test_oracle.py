@@ -20,6 +20,21 @@ def test_pin(pin):
     pin(_fwd, _bwd)
 
 
+@pytest.mark.parametrize("pin", oracle_pins.PARTIAL_PINS, ids=lambda p: p.__name__)
+def test_partial_pin(pin):
+    pin(oracle.attention_fwd_partial, oracle.merge_partials)
+
+
+def test_partial_at_equal_positions_is_plain_attention():
+    rng = np.random.default_rng(7)
+    q, k, v = (rng.standard_normal((1, 2, 9, 4)) for _ in range(3))
+    for causal in (False, True):
+        o, l = oracle.attention_fwd_partial(q, k, v, 0.5, causal, 3, 3)
+        ro, rl = oracle.attention_fwd(q, k, v, 0.5, causal)
+        np.testing.assert_allclose(o, ro, atol=1e-13, rtol=0)
+        np.testing.assert_allclose(l, rl, atol=1e-13, rtol=0)
+
+
 def test_pins_hold_with_small_row_blocks():
     """Row blocking is a memory device only: every pin holds when S is built
     two rows at a time."""

@@ -153,3 +153,38 @@ def test_unmutated_backward_copy_passes():
 def test_backward_mutant_is_caught(name):
     failed = _some_pin_fails(_fwd, _bwd_copy(name), oracle_pins.BACKWARD_PINS)
     assert failed, f"mutant {name} passed every backward pin"
+
+
+# ------------------------------------------------------------ partial / merge mutants
+
+def _merge_swapped(o_a, lse_a, o_b, lse_b):
+    o, l = oa.merge_partials(o_a, lse_a, o_b, lse_b)
+    m = np.maximum(lse_a, lse_b)
+    wa = np.exp(lse_b - m)                              # planted: weights swapped
+    wb = np.exp(lse_a - m)
+    return (wa[..., None] * o_a + wb[..., None] * o_b) / (wa + wb)[..., None], l
+
+
+def _merge_max_only(o_a, lse_a, o_b, lse_b):
+    o, _ = oa.merge_partials(o_a, lse_a, o_b, lse_b)
+    return o, np.maximum(lse_a, lse_b)                  # planted: LSE not summed
+
+
+def _partial_shifted(q, k, v, scale, causal, q_pos=0, k_pos=0):
+    return oa.attention_fwd_partial(q, k, v, scale, causal, q_pos + 1, k_pos)  # off by one
+
+
+@pytest.mark.parametrize("name,part,merge", [
+    ("merge_swapped", oa.attention_fwd_partial, _merge_swapped),
+    ("merge_max_only", oa.attention_fwd_partial, _merge_max_only),
+    ("partial_shifted", _partial_shifted, oa.merge_partials),
+])
+def test_partial_mutant_is_caught(name, part, merge):
+    failed = []
+    for pin in oracle_pins.PARTIAL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(part, merge)
+        except (AssertionError, FloatingPointError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every partial pin"
