@@ -57,6 +57,8 @@ def kernel_algorithmic(w):
         "bwd_delta": ("hbm", 2.0 * w.B * w.H * w.N * w.D * el + 4.0 * w.B * w.H * w.N),
         "bwd_dkdv": ("mfma", 4 * unit),      # S, dP, dV, dK
         "bwd_dq": ("mfma", 1 * unit),        # dQ
+        # merge of two partials: read O, O_part, LSE, LSE_part; write O, LSE
+        "merge": ("hbm", 3.0 * w.B * w.H * w.N * (w.D * el + 4)),
     }
 
 
@@ -65,6 +67,7 @@ KERNEL_SOURCES = {
     "bwd_delta": ["fa_bwd.hip", "fa_device.h"],
     "bwd_dkdv": ["fa_bwd.hip", "fa_device.h"],
     "bwd_dq": ["fa_bwd.hip", "fa_device.h"],
+    "merge": ["fa_merge.hip", "fa_device.h"],
 }
 
 
@@ -155,6 +158,73 @@ def run_gpu(w, steps, warmup):
     fa.fa_timing_enable(False)
     log(f"[bench] {steps} steps in {total_ms:.3f} ms")
     return total_ms / steps, kernels
+
+
+def run_split(w, parts, reps=3):
+    """The forward of workload `w` assembled from `parts` query blocks and
+    `parts` key/value blocks, as `parts` devices holding one block each would
+    compute it: every query block attends to each visible key block with
+    fa_fwd_partial and folds the results together with fa_merge.  Blocks are
+    copied to contiguous buffers before timing (each device would hold its
+    own).  Returns the assembled forward's time and rate (credited with the
+    whole forward's flops) and the merge kernel's measured bandwidth."""
+    import torch
+    from exact_io_aware_58_amd import fa, inputs
+
+    devs = {n: upload(raw, w.dtype) for n, (_, raw) in inputs.make_inputs(w).items()
+            if n in ("q", "k", "v")}
+    code = {"f32": fa.FA_F32, "bf16": fa.FA_BF16, "f16": fa.FA_F16}[w.dtype]
+    nb = w.N // parts
+    qs, ks, vs = ([devs[n][:, :, i * nb:(i + 1) * nb].contiguous() for i in range(parts)]
+                  for n in ("q", "k", "v"))
+    del devs
+    acc_o = [torch.empty_like(qs[0]) for _ in range(parts)]
+    acc_l = [torch.empty((w.B, w.H, nb), dtype=torch.float32, device="cuda") for _ in range(parts)]
+    tmp_o, tmp_l = torch.empty_like(qs[0]), torch.empty_like(acc_l[0])
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def forward():
+        for s_ in range(parts):
+            for t in range(parts):
+                if w.causal and t > s_:
+                    break
+                first = t == 0
+                o, l = (acc_o[s_], acc_l[s_]) if first else (tmp_o, tmp_l)
+                rc = fa.fa_fwd_partial(code, w.B, w.H, nb, nb, w.D, w.scale, w.causal,
+                                       s_ * nb, t * nb, qs[s_].data_ptr(), ks[t].data_ptr(),
+                                       vs[t].data_ptr(), o.data_ptr(), l.data_ptr(), sh)
+                if rc != fa.FA_OK:
+                    raise fa.FAError(rc, "fa_fwd_partial")
+                if not first:
+                    rc = fa.fa_merge(code, w.B, w.H, nb, w.D, acc_o[s_].data_ptr(),
+                                     acc_l[s_].data_ptr(), tmp_o.data_ptr(), tmp_l.data_ptr(), sh)
+                    if rc != fa.FA_OK:
+                        raise fa.FAError(rc, "fa_merge")
+
+    forward()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fa.fa_timing_enable(True)
+    e0.record()
+    for _ in range(reps):
+        forward()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    n, mms, _ = fa.fa_timing_read(fa.FA_KERNEL_MERGE)
+    fa.fa_timing_enable(False)
+    f, _ = flops(w)
+    sub = type(w)(w.name, w.seed, w.B, w.H, nb, w.D, w.dtype, w.causal, False)
+    _, merge_bytes = kernel_algorithmic(sub)["merge"]
+    merge_ms = mms / n if n else None
+    return {
+        "workload": f"{w.name} forward from {parts} query x {parts} key blocks",
+        "ms": ms, "tflops": f / (ms / 1e3) / 1e12,
+        "merge": {"launches_per_forward": n // reps if n else 0, "avg_ms": merge_ms,
+                  "GB/s": merge_bytes / (merge_ms / 1e3) / 1e9 if merge_ms else None,
+                  "frac_of_hbm_peak": (merge_bytes / (merge_ms / 1e3) / 1e9 / PEAK_HBM_GBS)
+                  if merge_ms else None},
+    }
 
 
 def cpu_baseline(w, rows):
@@ -271,7 +341,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=32768,
                     help="rows of the oracle sample timed for cpu_baseline (0: skip)")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the N=16384 D=128 forward-only figure")
+                    help="skip the N=16384 D=128 forward-only figure and the block-split "
+                         "forward")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size kernel for scaling HBM byte counters)")
@@ -325,6 +396,11 @@ def main():
                      "tflops": f4 / (ms4 / 1e3) / 1e12,
                      "pct_of_bf16_peak": 100.0 * f4 / (ms4 / 1e3) / 1e12 / PEAK_BF16_TFLOPS}
 
+    split = None
+    if not args.no_secondary and w.N % 4 == 0:
+        split = run_split(w, 4)
+        log(f"[bench] split forward: {split['ms']:.3f} ms")
+
     if args.copy_mib > 0:
         import torch
         n = args.copy_mib * (1 << 20) // 4
@@ -364,6 +440,8 @@ def main():
     }
     if secondary:
         out["fwd_n16384_d128"] = secondary
+    if split:
+        out["split_fwd"] = split
     print(json.dumps(out), flush=True)
 
 

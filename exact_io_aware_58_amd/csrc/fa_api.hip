@@ -11,6 +11,10 @@
 namespace {
 
 constexpr int kMaxN = 1 << 23;  // one head's tensor stays below 4 GiB (buffer range)
+// B*H*N rows at most: every grid stays below 2^32 work-items (and the
+// tensors far beyond one GPU's memory before that).
+constexpr double kMaxRows = 1073741824.0;  // 2^30
+constexpr long long kMaxPos = 1LL << 62;    // partial attention positions
 
 bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -19,11 +23,7 @@ int check_problem(int dtype, int B, int H, int N, int D, float scale) {
   if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_UNSUPPORTED;
   if (B <= 0 || H <= 0 || N <= 0 || N > kMaxN) return FA_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-  // element count and every launch's grid must fit the index types used
-  const double elems = (double)B * H * N * D;
-  if (elems > 9.0e18 / 4) return FA_ERR_INVALID_ARG;
-  const double tiles = (double)B * H * ((N + 63) / 64);
-  if (tiles > 2.0e9) return FA_ERR_INVALID_ARG;
+  if ((double)B * H * N > kMaxRows) return FA_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }
@@ -35,7 +35,7 @@ size_t delta_bytes(int B, int H, int N) {
 
 }  // namespace
 
-extern "C" int fa_version(void) { return 1; }
+extern "C" int fa_version(void) { return 2; }
 
 extern "C" const char* fa_status_string(int status) {
   switch (status) {
@@ -55,12 +55,56 @@ extern "C" int fa_fwd(int dtype, int B, int H, int N, int D, float scale, int ca
   if (rc != FA_OK) return rc;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
     return FA_ERR_INVALID_ARG;
-  fa::FwdArgs a{dtype, B, H, N, D, scale, causal ? 1 : 0, Q, K, V, O, LSE,
+  fa::FwdArgs a{dtype, B, H, N, N, D, 0, scale, causal ? 1 : 0, Q, K, V, O, LSE,
                 (hipStream_t)stream};
   hipError_t e;
   {
     fa::TimedLaunch t(FA_KERNEL_FWD, a.stream);
     e = fa::launch_fwd(a);
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int fa_fwd_partial(int dtype, int B, int H, int Nq, int Nk, int D, float scale,
+                              int causal, long long q_pos, long long k_pos, const void* Q,
+                              const void* K, const void* V, void* O, float* LSE,
+                              void* stream) {
+  int rc = check_problem(dtype, B, H, Nq, D, scale);
+  if (rc != FA_OK) return rc;
+  rc = check_problem(dtype, B, H, Nk, D, scale);
+  if (rc != FA_OK) return rc;
+  if (q_pos < 0 || k_pos < 0 || q_pos > kMaxPos || k_pos > kMaxPos) return FA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
+    return FA_ERR_INVALID_ARG;
+  // Key j is visible to query i iff k_pos + j <= q_pos + i, i.e. j <= i + d.
+  // d >= Nk - 1 makes every key visible (the unmasked kernels); d <= -Nq
+  // hides every key, and any such d behaves like -Nq.
+  long long d = q_pos - k_pos;
+  int mask = causal ? 1 : 0;
+  if (mask && d >= (long long)Nk - 1) mask = 0;
+  if (d < -(long long)Nq) d = -(long long)Nq;
+  if (d > (long long)Nk) d = Nk;
+  fa::FwdArgs a{dtype, B, H, Nq, Nk, D, (int)d, scale, mask, Q, K, V, O, LSE,
+                (hipStream_t)stream};
+  hipError_t e;
+  {
+    fa::TimedLaunch t(FA_KERNEL_FWD, a.stream);
+    e = fa::launch_fwd(a);
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int fa_merge(int dtype, int B, int H, int N, int D, void* O, float* LSE,
+                        const void* O_part, const float* LSE_part, void* stream) {
+  int rc = check_problem(dtype, B, H, N, D, 1.f);
+  if (rc != FA_OK) return rc;
+  if (!aligned16(O) || !aligned16(LSE) || !aligned16(O_part) || !aligned16(LSE_part))
+    return FA_ERR_INVALID_ARG;
+  fa::MergeArgs a{dtype, B, H, N, D, O, LSE, O_part, LSE_part, (hipStream_t)stream};
+  hipError_t e;
+  {
+    fa::TimedLaunch t(FA_KERNEL_MERGE, a.stream);
+    e = fa::launch_merge(a);
   }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -54,20 +54,25 @@ bwd_delta_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO
                  float* __restrict__ lse2, size_t rows) {
   constexpr int TPR = D / 8;  // threads per row, 16 bytes each
   constexpr int RPB = 256 / TPR;
-  const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int part = threadIdx.x % TPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const u32x4 o = ld_global16(O + row * D + part * 8);
-    const u32x4 g = ld_global16(dO + row * D + part * 8);
+  // Grid-stride over rows; every lane of a wave runs the same number of
+  // iterations (the bound is per workgroup), so the shuffles stay converged.
+  for (size_t row0 = (size_t)blockIdx.x * RPB; row0 < rows; row0 += (size_t)gridDim.x * RPB) {
+    const size_t row = row0 + threadIdx.x / TPR;
+    float acc = 0.f;
+    if (row < rows) {
+      const u32x4 o = ld_global16(O + row * D + part * 8);
+      const u32x4 g = ld_global16(dO + row * D + part * 8);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc = fmaf(T::to_float(elem16(o, j)), T::to_float(elem16(g, j)), acc);
-  }
+      for (int j = 0; j < 8; ++j)
+        acc = fmaf(T::to_float(elem16(o, j)), T::to_float(elem16(g, j)), acc);
+    }
 #pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && part == 0) {
-    delta[row] = acc;
-    lse2[row] = LSE[row] * kLog2e;
+    for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (row < rows && part == 0) {
+      delta[row] = acc;
+      lse2[row] = LSE[row] * kLog2e;
+    }
   }
 }
 
@@ -500,7 +505,8 @@ template <typename T>
 static hipError_t delta16(const BwdArgs& a) {
   const size_t rows = (size_t)a.B * a.H * a.N;
   const int rpb = 256 / (a.D / 8);
-  const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
+  const size_t blocks = (rows + rpb - 1) / rpb;
+  const unsigned grid = (unsigned)(blocks < (1u << 20) ? blocks : (1u << 20));
   if (a.D == 64)
     hipLaunchKernelGGL((bwd_delta_kernel<T, 64>), dim3(grid), dim3(256), 0, a.stream,
                        (const uint16_t*)a.O, (const uint16_t*)a.dO, a.LSE, a.delta, a.lse2, rows);

@@ -84,6 +84,21 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // True on every lane when any lane of the wave has `pred` set.
 __device__ inline bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 
+// s when off <= lim, else `ninf` (-inf held in a VGPR); `off` is a
+// compile-time constant after unrolling.  The compare and the select sit in
+// one asm block, so masking a tile never keeps dozens of lane masks alive in
+// scalar registers at once (left to itself the compiler hoists all the
+// compares of a tile and spills their masks).  s_nop 1: the wait states a
+// VALU write of VCC needs before a VALU reads it as a lane mask.
+__device__ __forceinline__ float keep_if_le(float s, int lim, int off, float ninf) {
+  float r;
+  asm("v_cmp_gt_i32_e32 vcc, %2, %1\n\ts_nop 1\n\tv_cndmask_b32_e32 %0, %3, %4, vcc"
+      : "=v"(r)
+      : "v"(lim), "i"(off), "v"(s), "v"(ninf)
+      : "vcc");
+  return r;
+}
+
 // ---- buffer loads ----
 // A raw buffer resource over one (batch, head) slab: loads whose byte offset
 // is at or past `bytes` return zeros instead of touching memory, which masks

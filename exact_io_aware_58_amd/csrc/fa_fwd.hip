@@ -35,6 +35,7 @@
 //     for the mask, and the longest query blocks are launched first.
 #include <hip/hip_runtime.h>
 
+#include <float.h>
 #include <math.h>
 
 #include <type_traits>
@@ -58,11 +59,38 @@ struct FwdTile<128> {
 constexpr int kFwdBR = 128;  // query rows per workgroup (4 waves x 32)
 constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay <= 256
 
+// Sets the scores of invisible keys to -inf.  Register r of block kb holds
+// key ts + 4hh + 32kb + 8(r/4) + r%4; keys at or past Nk, and (causal) past
+// `last` (the lane's last visible key), are dropped.  The first form keeps
+// each compare next to its select (see keep_if_le): left to the compiler,
+// the compares of a 128-key tile (D = 64) or a causal tile are all hoisted
+// and their masks spilled.  The 64-key unmasked-causal tiles (D = 128) keep
+// the plain form, which compiles without spills.
+template <bool CAUSAL, int NKB>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[NKB], int ts, int Nk, int last, int hh) {
+  if constexpr (CAUSAL || NKB == 4) {
+    const int lim = (CAUSAL ? min(Nk - 1, last) : Nk - 1) - ts - 4 * hh;
+    const float ninf = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        s[kb][r] = keep_if_le(s[kb][r], lim, kb * 32 + 8 * (r >> 2) + (r & 3), ninf);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (ts + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3) >= Nk) s[kb][r] = -INFINITY;
+  }
+}
+
 template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2)
 fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
              const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-             float* __restrict__ LSE, int N, float c, int nqt, int total) {
+             float* __restrict__ LSE, int Nq, int Nk, int dlt, float c, int nqt,
+             int total) {
   constexpr int BC = FwdTile<D>::BC;
   constexpr int TILE = BC * D;             // elements of one K or V tile
   constexpr int BLOCKS = TILE * 2 / 1024;  // 1 KiB blocks per tile
@@ -92,11 +120,12 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int wq0 = q0 + wave * 32;
   const int myq = wq0 + l32;
 
-  const size_t base = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto rQ = make_rsrc(Q + base, head_bytes);
-  const i32x4 rK = rsrc_words(K + base, head_bytes);  // direct-to-LDS sources
-  const i32x4 rV = rsrc_words(V + base, head_bytes);
+  const size_t qbase = (size_t)bh * (size_t)Nq * D;
+  const size_t kbase = (size_t)bh * (size_t)Nk * D;
+  const auto rQ = make_rsrc(Q + qbase, (uint32_t)Nq * D * 2);
+  const uint32_t kv_bytes = (uint32_t)Nk * D * 2;
+  const i32x4 rK = rsrc_words(K + kbase, kv_bytes);  // direct-to-LDS sources
+  const i32x4 rV = rsrc_words(V + kbase, kv_bytes);
 
   // B operand of S^T = K Q^T: lane (l32, hh) holds Q[myq][16c + 8hh .. +7]
   // (zeros past the last row).
@@ -122,7 +151,8 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int t = 0; t < 2; ++t)
       voff[db][t] = toff<D>(8 * t + 4 * (G >> 1) + (a16 >> 2), 32 * db + 16 * (G & 1) + 4 * (a16 & 3));
 
-  const int kend = CAUSAL ? min(N, q0 + kFwdBR) : N;
+  // Causal: key j is visible to query i iff j <= i + dlt.
+  const int kend = CAUSAL ? max(0, min(Nk, q0 + kFwdBR + dlt)) : Nk;
   const int ntiles = (kend + BC - 1) / BC;
 
   // Direct global->LDS loads of one key tile into a stage (K then V).
@@ -146,7 +176,10 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // moved when a tile's maximum exceeds it by more than kRescaleSlack, so the
   // rescale of O and l (exact in any case: O and l always share the
   // reference) is rare; weights then stay below 2^kRescaleSlack.
-  float m = -INFINITY;
+  // It starts at the lowest finite float, not -inf: a row that sees no key
+  // (possible with a position offset) then keeps weights exp2(-inf) = 0 and
+  // rescale factors exp2(0) = 1 instead of NaN.
+  float m = -FLT_MAX;
   float lpart = 0.f;
 
   // MASKED: ragged tail or causal-diagonal tile (per-wave skip, element
@@ -154,7 +187,7 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   auto tile = [&](const uint16_t* Ks, int ts, auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
     const uint16_t* Vs = Ks + TILE;
-    if (!MASKED || !CAUSAL || ts <= wq0 + 31) {
+    if (!MASKED || !CAUSAL || ts <= wq0 + 31 + dlt) {
       // S^T[key][q] for the wave's 32 queries and the tile's BC keys.
       f32x16 s[NKB];
 #pragma unroll
@@ -166,16 +199,8 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
           s[kb] = T::mfma(ld_lds16(Ks + kb * 32 * D + koff[cc]), qf[cc], s[kb]);
-      const bool need_mask = MASKED && ((ts + BC > N) || (CAUSAL && ts + BC - 1 > wq0));
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = ts + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key >= N || (CAUSAL && key > myq)) s[kb][r] = -INFINITY;
-          }
-      }
+      const bool need_mask = MASKED && ((ts + BC > Nk) || (CAUSAL && ts + BC - 1 > wq0 + dlt));
+      if (need_mask) mask_tile<CAUSAL, NKB>(s, ts, Nk, myq + dlt, hh);
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -222,7 +247,7 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   // Tiles visible to every row (no tail, not past the causal diagonal):
   // straight-line body, double-buffered; the rest (at the end): masked body.
-  const int nfull = min(N / BC, CAUSAL ? (q0 + 1) / BC : ntiles);
+  const int nfull = min(Nk / BC, CAUSAL ? max(0, q0 + dlt + 1) / BC : ntiles);
   int t = 0;
   if (nfull > 0) dma(smem0, 0);
   wait_dma();
@@ -251,10 +276,11 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 
   // Epilogue: one division by the full row sum, then bf16/f16 (RNE) stores.
+  // A row with no visible key has ltot = 0: O = 0 and LSE = -inf.
   const float ltot = sum_halves(lpart);
-  const float inv = 1.f / ltot;
-  if (myq < N) {
-    uint16_t* Oq = O + base + (size_t)myq * D;
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  if (myq < Nq) {
+    uint16_t* Oq = O + qbase + (size_t)myq * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -264,7 +290,7 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         w[1] = T::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
         st_global8(Oq + db * 32 + 8 * g + 4 * hh, w);
       }
-    if (hh == 0) LSE[(size_t)bh * N + myq] = (m + log2f(ltot)) * kLn2;
+    if (hh == 0) LSE[(size_t)bh * Nq + myq] = (m + log2f(ltot)) * kLn2;
   }
 }
 
@@ -285,7 +311,8 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
                                              const uint16_t* __restrict__ K,
                                              const uint16_t* __restrict__ V,
                                              uint16_t* __restrict__ O, float* __restrict__ LSE,
-                                             int N, float c, int nqt, int total, uint16_t* kb0,
+                                             int Nq, int Nk, int dlt, float c, int nqt,
+                                             int total, uint16_t* kb0,
                                              uint16_t* kb1, uint16_t* vb0, uint16_t* vb1) {
   constexpr int BC = FwdTile<D>::BC;
   constexpr int TILE = BC * D;
@@ -309,11 +336,12 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
   const int wq0 = q0 + wave * 32;
   const int myq = wq0 + l32;
 
-  const size_t base = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto rQ = make_rsrc(Q + base, head_bytes);
-  const i32x4 rK = rsrc_words(K + base, head_bytes);  // direct-to-LDS sources
-  const i32x4 rV = rsrc_words(V + base, head_bytes);
+  const size_t qbase = (size_t)bh * (size_t)Nq * D;
+  const size_t kbase = (size_t)bh * (size_t)Nk * D;
+  const auto rQ = make_rsrc(Q + qbase, (uint32_t)Nq * D * 2);
+  const uint32_t kv_bytes = (uint32_t)Nk * D * 2;
+  const i32x4 rK = rsrc_words(K + kbase, kv_bytes);  // direct-to-LDS sources
+  const i32x4 rV = rsrc_words(V + kbase, kv_bytes);
 
   u32x4 qf[NDC];
 #pragma unroll
@@ -332,7 +360,7 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
     for (int t = 0; t < 2; ++t)
       voff[db][t] = toff<D>(8 * t + 4 * (G >> 1) + (a16 >> 2), 32 * db + 16 * (G & 1) + 4 * (a16 & 3));
 
-  const int kend = CAUSAL ? min(N, q0 + kPpBR) : N;
+  const int kend = CAUSAL ? max(0, min(Nk, q0 + kPpBR + dlt)) : Nk;
   const int ntiles = (kend + BC - 1) / BC;
 
   auto dma_tile = [&](const uint16_t* dst, const i32x4& r, int ts) {
@@ -348,12 +376,12 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m = -INFINITY;  // reference max (log2 units), moved lazily
+  float m = -FLT_MAX;  // reference max (log2 units), moved lazily; see fwd16_kernel
   float lpart = 0.f;    // partial row sum over this lane's keys
   f32x16 s[NKB];        // scores of the tile between its M and X phases
   u32x4 pk[NKC];        // probabilities between X(j) and M(j+1)
 
-  auto active = [&](int j) { return !CAUSAL || j * BC <= wq0 + 31; };
+  auto active = [&](int j) { return !CAUSAL || j * BC <= wq0 + 31 + dlt; };
 
   auto phase_m = [&](int j, const uint16_t* Kcur, const uint16_t* Vprev) {
     // Independent accumulators are interleaved (reduction step outer) so
@@ -384,16 +412,8 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
   auto phase_x = [&](int j) {
     if (j < 0 || j >= ntiles || !active(j)) return;
     const int ts = j * BC;
-    const bool need_mask = (ts + BC > N) || (CAUSAL && ts + BC - 1 > wq0);
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = ts + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key >= N || (CAUSAL && key > myq)) s[kb][r] = -INFINITY;
-        }
-    }
+    const bool need_mask = (ts + BC > Nk) || (CAUSAL && ts + BC - 1 > wq0 + dlt);
+    if (need_mask) mask_tile<CAUSAL, NKB>(s, ts, Nk, myq + dlt, hh);
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -446,10 +466,11 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
     barrier_after_loads();
   }
 
+  // A row with no visible key has ltot = 0: O = 0 and LSE = -inf.
   const float ltot = sum_halves(lpart);
-  const float inv = 1.f / ltot;
-  if (myq < N) {
-    uint16_t* Oq = O + base + (size_t)myq * D;
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  if (myq < Nq) {
+    uint16_t* Oq = O + qbase + (size_t)myq * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -459,7 +480,7 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
         w[1] = T::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
         st_global8(Oq + db * 32 + 8 * g + 4 * hh, w);
       }
-    if (hh == 0) LSE[(size_t)bh * N + myq] = (m + log2f(ltot)) * kLn2;
+    if (hh == 0) LSE[(size_t)bh * Nq + myq] = (m + log2f(ltot)) * kLn2;
   }
 }
 
@@ -467,7 +488,8 @@ template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(512, 1)
 fwd16pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-               float* __restrict__ LSE, int N, float c, int nqt, int total) {
+               float* __restrict__ LSE, int Nq, int Nk, int dlt, float c, int nqt,
+               int total) {
   constexpr int TILE = FwdTile<D>::BC * D;
   // Separate buffers with compile-time selection (the slot loop is unrolled
   // over two tiles): loads into one buffer never alias reads of another.
@@ -477,9 +499,11 @@ fwd16pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   __shared__ __attribute__((aligned(1024))) uint16_t vb1[TILE];
   // Each group runs its own copy of the slot loop (no per-slot branch on it).
   if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 8) == 0)
-    fwd16pp_body<T, D, CAUSAL, 0>(Q, K, V, O, LSE, N, c, nqt, total, kb0, kb1, vb0, vb1);
+    fwd16pp_body<T, D, CAUSAL, 0>(Q, K, V, O, LSE, Nq, Nk, dlt, c, nqt, total, kb0, kb1, vb0,
+                                  vb1);
   else
-    fwd16pp_body<T, D, CAUSAL, 1>(Q, K, V, O, LSE, N, c, nqt, total, kb0, kb1, vb0, vb1);
+    fwd16pp_body<T, D, CAUSAL, 1>(Q, K, V, O, LSE, Nq, Nk, dlt, c, nqt, total, kb0, kb1, vb0,
+                                  vb1);
 }
 
 // fp32 kernel: true fp32 products on the vector ALUs (no reduced-precision
@@ -492,7 +516,8 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256)
 fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
              const float* __restrict__ V, float* __restrict__ O,
-             float* __restrict__ LSE, int N, float c, int nqt, int total) {
+             float* __restrict__ LSE, int Nq, int Nk, int dlt, float c, int nqt,
+             int total) {
   constexpr int BK = 32;
   constexpr int DP = D / 4;
   __shared__ __attribute__((aligned(16))) float Ks[BK * D];
@@ -506,16 +531,17 @@ fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   if (CAUSAL) qt = nqt - 1 - qt;
   const int q0 = qt * kF32BR;
   const int myq = q0 + qi;
-  const size_t base = (size_t)bh * (size_t)N * D;
+  const size_t qbase = (size_t)bh * (size_t)Nq * D;
+  const size_t kbase = (size_t)bh * (size_t)Nk * D;
 
   float q[DP], o[DP];
 #pragma unroll
   for (int e = 0; e < DP; ++e) {
-    q[e] = myq < N ? Q[base + (size_t)myq * D + part * DP + e] : 0.f;
+    q[e] = myq < Nq ? Q[qbase + (size_t)myq * D + part * DP + e] : 0.f;
     o[e] = 0.f;
   }
-  float m = -INFINITY, l = 0.f;
-  const int kend = CAUSAL ? min(N, q0 + kF32BR) : N;
+  float m = -FLT_MAX, l = 0.f;  // finite start: rows that see no key stay NaN-free
+  const int kend = CAUSAL ? max(0, min(Nk, q0 + kF32BR + dlt)) : Nk;
 
   for (int ts = 0; ts < kend; ts += BK) {
     __syncthreads();
@@ -523,9 +549,9 @@ fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
       const int row = (i * 4) / D, col = (i * 4) % D;
       const int key = ts + row;
       f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-      if (key < N) {
-        kv = *reinterpret_cast<const f32x4*>(K + base + (size_t)key * D + col);
-        vv = *reinterpret_cast<const f32x4*>(V + base + (size_t)key * D + col);
+      if (key < Nk) {
+        kv = *reinterpret_cast<const f32x4*>(K + kbase + (size_t)key * D + col);
+        vv = *reinterpret_cast<const f32x4*>(V + kbase + (size_t)key * D + col);
       }
       *reinterpret_cast<f32x4*>(Ks + row * D + col) = kv;
       *reinterpret_cast<f32x4*>(Vs + row * D + col) = vv;
@@ -542,7 +568,7 @@ fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
       acc += __shfl_xor(acc, 1, 64);
       acc += __shfl_xor(acc, 2, 64);
       const int key = ts + j;
-      if (key >= N || (CAUSAL && key > myq)) acc = -INFINITY;
+      if (key >= Nk || (CAUSAL && key > myq + dlt)) acc = -INFINITY;
       s[j] = acc;
       mx = fmaxf(mx, acc);
     }
@@ -560,40 +586,41 @@ fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
       for (int e = 0; e < DP; ++e) o[e] = fmaf(p, Vs[j * D + part * DP + e], o[e]);
     }
   }
-  if (myq < N) {
-    const float inv = 1.f / l;
+  if (myq < Nq) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;  // no visible key: O = 0, LSE = -inf
 #pragma unroll
-    for (int e = 0; e < DP; ++e) O[base + (size_t)myq * D + part * DP + e] = o[e] * inv;
-    if (part == 0) LSE[(size_t)bh * N + myq] = (m + log2f(l)) * kLn2;
+    for (int e = 0; e < DP; ++e) O[qbase + (size_t)myq * D + part * DP + e] = o[e] * inv;
+    if (part == 0) LSE[(size_t)bh * Nq + myq] = (m + log2f(l)) * kLn2;
   }
 }
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch16(const FwdArgs& a) {
   // Enough 256-row workgroups to give every CU at least two: ping-pong kernel.
-  const int npp = (a.N + kPpBR - 1) / kPpBR;
+  const int npp = (a.Nq + kPpBR - 1) / kPpBR;
   if ((long)npp * a.B * a.H >= 512) {
     const int total = npp * a.B * a.H;
     hipLaunchKernelGGL((fwd16pp_kernel<T, D, CAUSAL>), dim3(total), dim3(512), 0, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                       (uint16_t*)a.O, a.LSE, a.N, a.scale * kLog2e, npp, total);
+                       (uint16_t*)a.O, a.LSE, a.Nq, a.Nk, a.delta, a.scale * kLog2e, npp,
+                       total);
     return hipGetLastError();
   }
-  const int nqt = (a.N + kFwdBR - 1) / kFwdBR;
+  const int nqt = (a.Nq + kFwdBR - 1) / kFwdBR;
   const int total = nqt * a.B * a.H;
   hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
                      (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                     (uint16_t*)a.O, a.LSE, a.N, a.scale * kLog2e, nqt, total);
+                     (uint16_t*)a.O, a.LSE, a.Nq, a.Nk, a.delta, a.scale * kLog2e, nqt, total);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 static hipError_t launch32(const FwdArgs& a) {
-  const int nqt = (a.N + kF32BR - 1) / kF32BR;
+  const int nqt = (a.Nq + kF32BR - 1) / kF32BR;
   const int total = nqt * a.B * a.H;
   hipLaunchKernelGGL((fwd32_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
                      (const float*)a.Q, (const float*)a.K, (const float*)a.V, (float*)a.O,
-                     a.LSE, a.N, a.scale * kLog2e, nqt, total);
+                     a.LSE, a.Nq, a.Nk, a.delta, a.scale * kLog2e, nqt, total);
   return hipGetLastError();
 }
 

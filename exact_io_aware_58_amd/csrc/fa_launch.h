@@ -10,7 +10,10 @@ namespace fa {
 enum Dtype { kF32 = 0, kBF16 = 1, kF16 = 2 };
 
 struct FwdArgs {
-  int dtype, B, H, N, D;
+  int dtype, B, H;
+  int Nq, Nk;  // query rows and key rows per head
+  int D;
+  int delta;   // causal: key j is visible to query i iff j <= i + delta
   float scale;
   int causal;
   const void *Q, *K, *V;
@@ -31,7 +34,17 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+struct MergeArgs {
+  int dtype, B, H, N, D;
+  void* O;           // [B, H, N, D], partial a on entry, merged result on exit
+  float* LSE;        // [B, H, N]
+  const void* Ob;    // partial b
+  const float* LSEb;
+  hipStream_t stream;
+};
+
 hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_merge(const MergeArgs& a);
 // Each backward launcher enqueues one kernel.
 hipError_t launch_bwd_delta(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);

@@ -116,6 +116,7 @@ extern "C" const char* fa_kernel_name(int kernel_id) {
     case FA_KERNEL_BWD_DELTA: return "bwd_delta";
     case FA_KERNEL_BWD_DKDV: return "bwd_dkdv";
     case FA_KERNEL_BWD_DQ: return "bwd_dq";
+    case FA_KERNEL_MERGE: return "merge";
     default: return "unknown";
   }
 }

@@ -18,12 +18,16 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
 FA_KERNEL_FWD, FA_KERNEL_BWD_DELTA, FA_KERNEL_BWD_DKDV, FA_KERNEL_BWD_DQ = 0, 1, 2, 3
-FA_KERNEL_COUNT = 4
+FA_KERNEL_MERGE = 4
+FA_KERNEL_COUNT = 5
 
 # Every symbol include/fa.h declares, with (restype, argtypes).
 _c_int, _c_size, _vp, _f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+_ll = ctypes.c_longlong
 SIGNATURES = {
     "fa_fwd": (_c_int, [_c_int] * 5 + [_f, _c_int] + [_vp] * 6),
+    "fa_fwd_partial": (_c_int, [_c_int] * 6 + [_f, _c_int, _ll, _ll] + [_vp] * 6),
+    "fa_merge": (_c_int, [_c_int] * 5 + [_vp] * 5),
     "fa_bwd_workspace_bytes": (_c_size, [_c_int] * 6),
     "fa_bwd": (_c_int, [_c_int] * 5 + [_f, _c_int] + [_vp] * 10 + [_c_size, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_c_int]),
@@ -61,6 +65,16 @@ _lib = _load()
 
 def fa_fwd(dtype, B, H, N, D, scale, causal, Q, K, V, O, LSE, stream) -> int:
     return _lib.fa_fwd(dtype, B, H, N, D, scale, int(causal), Q, K, V, O, LSE, stream)
+
+
+def fa_fwd_partial(dtype, B, H, Nq, Nk, D, scale, causal, q_pos, k_pos, Q, K, V, O, LSE,
+                   stream) -> int:
+    return _lib.fa_fwd_partial(dtype, B, H, Nq, Nk, D, scale, int(causal), q_pos, k_pos,
+                               Q, K, V, O, LSE, stream)
+
+
+def fa_merge(dtype, B, H, N, D, O, LSE, O_part, LSE_part, stream) -> int:
+    return _lib.fa_merge(dtype, B, H, N, D, O, LSE, O_part, LSE_part, stream)
 
 
 def fa_bwd_workspace_bytes(dtype, B, H, N, D, causal) -> int:
@@ -138,6 +152,46 @@ def forward(q, k, v, scale, causal=False, out=None, lse=None):
     if rc != FA_OK:
         raise FAError(rc, "fa_fwd")
     return out, lse
+
+
+def forward_partial(q, k, v, scale, causal=False, q_pos=0, k_pos=0, out=None, lse=None):
+    """(O, LSE) of (B, H, Nq, D) queries at positions q_pos.. over (B, H, Nk, D)
+    keys/values at positions k_pos..; rows that see no key get O = 0, LSE = -inf."""
+    import torch
+    _check_qkv(k, v)
+    if q.dim() != 4:
+        raise ValueError("expected (B, H, Nq, D) queries")
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if (not q.is_cuda or not q.is_contiguous() or q.dtype != k.dtype
+            or tuple(k.shape) != (B, H, Nk, D)):
+        raise ValueError("q must be a contiguous (B, H, Nq, D) device tensor matching k, v")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    rc = fa_fwd_partial(_dtype_code(q), B, H, Nq, Nk, D, float(scale), causal, int(q_pos),
+                        int(k_pos), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                        lse.data_ptr(), _stream())
+    if rc != FA_OK:
+        raise FAError(rc, "fa_fwd_partial")
+    return out, lse
+
+
+def merge(o, lse, o_part, lse_part):
+    """Merges (o_part, lse_part) into (o, lse) in place and returns them."""
+    import torch
+    _check_qkv(o, o_part)
+    B, H, N, D = o.shape
+    for t in (lse, lse_part):
+        if (not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != (B, H, N)
+                or t.dtype != torch.float32):
+            raise ValueError("LSE tensors must be contiguous float32 (B, H, N) device tensors")
+    rc = fa_merge(_dtype_code(o), B, H, N, D, o.data_ptr(), lse.data_ptr(), o_part.data_ptr(),
+                  lse_part.data_ptr(), _stream())
+    if rc != FA_OK:
+        raise FAError(rc, "fa_merge")
+    return o, lse
 
 
 def workspace_bytes(q, causal=False):

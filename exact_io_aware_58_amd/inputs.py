@@ -19,7 +19,9 @@ import math
 
 import numpy as np
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3}
+# q, k, v, do: attention inputs; oa, ob, la, lb: synthetic partial results
+# (outputs and log-sum-exps) for checking the merge on its own.
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3, "oa": 4, "ob": 5, "la": 6, "lb": 7}
 
 
 @dataclasses.dataclass(frozen=True)

@@ -14,7 +14,8 @@
  *   - Tensors are (batch B, heads H, sequence N, head dim D), contiguous,
  *     row stride D elements ([ijyty] "传统 Attention 的问题": the
  *     (batch, heads, seq_len, head_dim) layout).  Self-attention: queries and
- *     keys share N.
+ *     keys share N (fa_fwd_partial alone takes separate query and key
+ *     lengths).  B * H * N <= 2^30 rows per tensor.
  *   - All tensor pointers are DEVICE pointers owned by the caller and must be
  *     16-byte aligned.  The library never allocates, frees or synchronises;
  *     it only enqueues kernels on `stream` (a hipStream_t; NULL = the null
@@ -47,7 +48,8 @@ typedef enum {
 
 typedef enum {
   FA_OK = 0,
-  FA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, B/H/N <= 0, N > 2^23, bad scale        */
+  FA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, B/H/N <= 0, N > 2^23, B*H*N > 2^30,
+                               bad scale, negative position                                    */
   FA_ERR_UNSUPPORTED = -2,  /* D not in {64, 128} or unknown dtype                         */
   FA_ERR_WORKSPACE = -3,    /* backward workspace missing or smaller than required          */
   FA_ERR_HIP = -4           /* a kernel launch failed (hipGetLastError after the launch)    */
@@ -72,6 +74,50 @@ typedef enum {
 int fa_fwd(int dtype, int B, int H, int N, int D, float scale, int causal,
            const void* Q, const void* K, const void* V, void* O, float* LSE,
            void* stream);
+
+/*
+ * fa_fwd_partial -- attention of a block of Nq queries over a block of Nk
+ * keys that may sit at other sequence positions: query row i is at position
+ * q_pos + i, key row j at k_pos + j.  Same tiled online softmax as fa_fwd,
+ * with the causal rule on positions: key j is kept for query i iff
+ * k_pos + j <= q_pos + i.  The (O, LSE) pair it returns is the state the
+ * online softmax carries ([guanweilu] "FlashAttention 的三板斧", second
+ * technique), so results over disjoint key blocks combine exactly with
+ * fa_merge -- the building block for splitting the keys of one sequence
+ * over several passes or devices.  With Nq = Nk = N and q_pos = k_pos it
+ * computes exactly what fa_fwd computes.
+ *
+ *   Q       : [B, H, Nq, D] of `dtype`, read only.
+ *   K, V    : [B, H, Nk, D] of `dtype`, read only.
+ *   O       : [B, H, Nq, D] of `dtype`, written.
+ *   LSE     : [B, H, Nq] float32, written.  A query row that sees no key
+ *             (causal, q_pos + i < k_pos) gets O = 0 and LSE = -inf.
+ *   q_pos, k_pos : >= 0 and <= 2^62 (ignored when causal == 0).
+ *   1 <= Nq, Nk <= 2^23; D and dtypes as fa_fwd.
+ * Returns an fa_status.
+ */
+int fa_fwd_partial(int dtype, int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                   long long q_pos, long long k_pos, const void* Q, const void* K,
+                   const void* V, void* O, float* LSE, void* stream);
+
+/*
+ * fa_merge -- combines, in place, two partial results for the same queries
+ * over disjoint key sets (from fa_fwd_partial, fa_fwd or earlier merges):
+ *   LSE <- ln(e^LSE + e^LSE_part),
+ *   O   <- e^(LSE_old - LSE_new) O + e^(LSE_part - LSE_new) O_part,
+ * the online-softmax update of [guanweilu] "FlashAttention 的三板斧",
+ * second technique, applied to whole blocks.  A row whose two LSEs are both
+ * -inf becomes O = 0, LSE = -inf.  Exact up to rounding: merging partials
+ * over a split of the keys gives fa_fwd over all of them.
+ *
+ *   O       : [B, H, N, D] of `dtype`, read and written (partial a -> merged).
+ *   LSE     : [B, H, N] float32, read and written.
+ *   O_part  : [B, H, N, D] of `dtype`, read only (may equal O).
+ *   LSE_part: [B, H, N] float32, read only.
+ * Returns an fa_status.
+ */
+int fa_merge(int dtype, int B, int H, int N, int D, void* O, float* LSE, const void* O_part,
+             const float* LSE_part, void* stream);
 
 /*
  * Bytes of device workspace fa_bwd needs for this problem: two float32
@@ -117,7 +163,8 @@ int fa_version(void);
  * stream; fa_timing_read synchronises those events and returns, for one
  * kernel id, the number of timed launches and their summed duration in
  * milliseconds.  fa_timing_enable(1) also clears previous totals.  Events
- * come from a fixed pool of 8192 pairs created at enable time; launches
+ * come from a fixed pool of 8192 pairs created at enable time (fa_fwd and
+ * fa_fwd_partial both count as FA_KERNEL_FWD); launches
  * beyond it are not timed (counted in *dropped).
  */
 enum {
@@ -125,7 +172,8 @@ enum {
   FA_KERNEL_BWD_DELTA = 1,    /* backward: Delta = rowsum(dO * O)        */
   FA_KERNEL_BWD_DKDV = 2,     /* backward: dK, dV                        */
   FA_KERNEL_BWD_DQ = 3,       /* backward: dQ                            */
-  FA_KERNEL_COUNT = 4
+  FA_KERNEL_MERGE = 4,        /* fa_merge                                */
+  FA_KERNEL_COUNT = 5
 };
 int fa_timing_enable(int on);
 int fa_timing_read(int kernel_id, long long* launches, double* total_ms, long long* dropped);

@@ -20,7 +20,8 @@ def _declared():
 
 
 def test_header_declares_the_api():
-    assert {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string"} <= set(_declared())
+    assert {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_fwd_partial",
+            "fa_merge"} <= set(_declared())
 
 
 def test_library_exports_every_declared_symbol():
@@ -49,7 +50,7 @@ P = [A + 0x1000 * i for i in range(12)]
 
 
 def test_version_and_status_strings(fa):
-    assert fa.fa_version() >= 1
+    assert fa.fa_version() >= 2
     for code in (0, -1, -2, -3, -4):
         assert fa.fa_status_string(code) != "unknown status"
     assert fa.fa_status_string(99) == "unknown status"
@@ -63,6 +64,7 @@ def test_version_and_status_strings(fa):
     (dict(H=-1), -1),
     (dict(N=0), -1),
     (dict(N=1 << 25), -1),
+    (dict(B=1 << 10, H=1 << 10, N=1 << 11), -1),  # B*H*N > 2^30
     (dict(scale=0.0), -1),
     (dict(scale=-0.125), -1),
     (dict(scale=float("inf")), -1),
@@ -117,4 +119,49 @@ def test_timing_read_bounds(fa):
         fa.fa_timing_read(fa.FA_KERNEL_COUNT)
     n, ms, dropped = fa.fa_timing_read(fa.FA_KERNEL_FWD)
     assert n == 0 and ms == 0.0 and dropped == 0
-    assert [fa.fa_kernel_name(i) for i in range(4)] == ["fwd", "bwd_delta", "bwd_dkdv", "bwd_dq"]
+    assert [fa.fa_kernel_name(i) for i in range(5)] == ["fwd", "bwd_delta", "bwd_dkdv", "bwd_dq",
+                                                        "merge"]
+    assert fa.fa_kernel_name(fa.FA_KERNEL_COUNT) == "unknown"
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(dtype=7), -2),
+    (dict(D=96), -2),
+    (dict(Nq=0), -1),
+    (dict(Nk=0), -1),
+    (dict(Nk=1 << 24), -1),
+    (dict(Nq=1 << 24), -1),
+    (dict(q_pos=-1), -1),
+    (dict(k_pos=-5), -1),
+    (dict(k_pos=(1 << 62) + 1), -1),
+    (dict(scale=0.0), -1),
+    (dict(scale=float("nan")), -1),
+])
+def test_fwd_partial_rejects_bad_problem(fa, args, status):
+    kw = dict(dtype=fa.FA_BF16, Nq=100, Nk=300, D=64, scale=0.125, q_pos=0, k_pos=0)
+    kw.update(args)
+    rc = fa.fa_fwd_partial(kw["dtype"], 1, 2, kw["Nq"], kw["Nk"], kw["D"], kw["scale"], 1,
+                           kw["q_pos"], kw["k_pos"], P[0], P[1], P[2], P[3], P[4], None)
+    assert rc == status
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_fwd_partial_rejects_null_or_misaligned(fa, which):
+    for bad in (0, A + 8):
+        ptrs = P[:5]
+        ptrs[which] = bad
+        assert fa.fa_fwd_partial(fa.FA_BF16, 1, 2, 100, 300, 64, 0.125, 1, 0, 0, *ptrs,
+                                 None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_merge_validation(fa):
+    ok = (P[0], P[1], P[2], P[3])
+    assert fa.fa_merge(7, 1, 2, 100, 64, *ok, None) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_merge(fa.FA_BF16, 1, 2, 100, 80, *ok, None) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_merge(fa.FA_BF16, 1, 0, 100, 64, *ok, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_merge(fa.FA_BF16, 1, 2, 0, 64, *ok, None) == fa.FA_ERR_INVALID_ARG
+    for which in range(4):
+        for bad in (0, A + 4):
+            ptrs = list(ok)
+            ptrs[which] = bad
+            assert fa.fa_merge(fa.FA_F16, 1, 2, 100, 64, *ptrs, None) == fa.FA_ERR_INVALID_ARG
