@@ -247,31 +247,6 @@ __device__ inline u32x2 ld_lds_tr(const uint16_t* p) {
 }
 __device__ inline u32x4 cat(u32x2 lo, u32x2 hi) { return u32x4{lo[0], lo[1], hi[0], hi[1]}; }
 
-// ---- transposed tile staging ----
-// Position of key (or query) row `row` (a multiple of 4) inside a transposed
-// LDS tile.  Inside every 16-row chunk the four 4-row groups {0,1,2,3} are
-// stored at group positions {0,2,1,3}: the 8 consecutive positions a lane
-// reads for one 32x32x16 MFMA step (8*(l/32) .. +7 of the chunk) are then the
-// rows whose values sit in 8 consecutive accumulator registers of that lane
-// (rows 8*(r/4) + 4*(l/32) + r%4 of the 32x32 output layout).
-__device__ inline int tposition(int row) {
-  const int g = (row & 15) >> 2;
-  return (row & ~15) + (((g & 1) << 1) | (g >> 1)) * 4;
-}
-
-// Write a 4-row x 8-column block (r[e] = row e, columns col0 .. col0+7) into a
-// transposed tile T[col][position] with row stride `stride` elements.
-__device__ inline void store_transposed4(uint16_t* T, int stride, int col0, int pos,
-                                         const u32x4 (&r)[4]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    u32x2 w;
-    w[0] = elem16(r[0], j) | (elem16(r[1], j) << 16);
-    w[1] = elem16(r[2], j) | (elem16(r[3], j) << 16);
-    *reinterpret_cast<u32x2*>(T + (col0 + j) * stride + pos) = w;
-  }
-}
-
 // ---- workgroup order ----
 // Workgroups are dealt round-robin to the 8 XCDs (blockIdx.x % 8).  Remap so
 // that each XCD receives one contiguous range of logical tiles: tiles of the
