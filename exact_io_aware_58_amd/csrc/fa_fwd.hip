@@ -57,7 +57,57 @@ struct FwdTile<128> {
 };
 
 constexpr int kFwdBR = 128;  // query rows per workgroup (4 waves x 32)
-constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay <= 256
+// Bound on a lane's partial row sum over one tile; it bounds every weight.
+constexpr float kSumLimit = 65536.f;
+
+// Online softmax of one tile.  Exponentiates the scores against the
+// reference maximum m (log2 units) and packs them as the B operand of
+// O^T += V^T P^T (registers 8*half .. +7 of block kb are the 8 K-slots of
+// reduction step 2*kb + half), adding the lane's weights to lpart.  The
+// reference moves lazily: every weight is at most the lane's partial sum, so
+// while no lane's sum exceeds kSumLimit the weights are safely bounded and m
+// stays put.  Otherwise (always on a row's first tile, where m is still the
+// lowest finite float) the wave takes the tile maximum, rescales O and l to
+// it -- exact, since O and l always share the reference -- and exponentiates
+// again.  The row maximum is therefore off the common path.
+template <typename T, int NKB, int NDB>
+__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[NKB], u32x4 (&pk)[2 * NKB],
+                                             float& m, float& lpart, f32x16 (&oacc)[NDB],
+                                             float c) {
+  auto exp_pack = [&]() {
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = fast_exp2(fmaf(s[kb][8 * half + 2 * i], c, -m));
+          const float p1 = fast_exp2(fmaf(s[kb][8 * half + 2 * i + 1], c, -m));
+          rs += p0 + p1;
+          pk[2 * kb + half][i] = T::pack2(p0, p1);
+        }
+    return rs;
+  };
+  float rs = exp_pack();
+  if (wave_any(!(rs <= kSumLimit))) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    const float mnew = fmaxf(m, max_halves(mx) * c);
+    const float alpha = fast_exp2(m - mnew);  // 0 on the first tile
+    m = mnew;
+    lpart *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    rs = exp_pack();
+  }
+  lpart += rs;
+}
 
 // Sets the scores of invisible keys to -inf.  Register r of block kb holds
 // key ts + 4hh + 32kb + 8(r/4) + r%4; keys at or past Nk, and (causal) past
@@ -171,14 +221,11 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  // Reference maximum (log2 units) the exponents are taken against, and the
-  // partial row sum over the keys this lane holds.  The reference is only
-  // moved when a tile's maximum exceeds it by more than kRescaleSlack, so the
-  // rescale of O and l (exact in any case: O and l always share the
-  // reference) is rare; weights then stay below 2^kRescaleSlack.
-  // It starts at the lowest finite float, not -inf: a row that sees no key
-  // (possible with a position offset) then keeps weights exp2(-inf) = 0 and
-  // rescale factors exp2(0) = 1 instead of NaN.
+  // Reference maximum (log2 units) the exponents are taken against (moved
+  // lazily, see softmax_tile), and the partial row sum over the keys this
+  // lane holds.  It starts at the lowest finite float, not -inf: a row that
+  // sees no key (possible with a position offset) then keeps weights
+  // exp2(-inf) = 0 and rescale factors exp2(0) = 1 instead of NaN.
   float m = -FLT_MAX;
   float lpart = 0.f;
 
@@ -201,39 +248,8 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           s[kb] = T::mfma(ld_lds16(Ks + kb * 32 * D + koff[cc]), qf[cc], s[kb]);
       const bool need_mask = MASKED && ((ts + BC > Nk) || (CAUSAL && ts + BC - 1 > wq0 + dlt));
       if (need_mask) mask_tile<CAUSAL, NKB>(s, ts, Nk, myq + dlt, hh);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      const float mt = max_halves(mx) * c;  // tile row max, log2 units
-      if (wave_any(mt > m + kRescaleSlack)) {
-        const float mnew = fmaxf(m, mt);
-        const float alpha = fast_exp2(m - mnew);  // 0 on the first tile
-        m = mnew;
-        lpart *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-
-      // P^T as the B operand of O^T += V^T P^T (registers 8*half .. +7 of
-      // block kb are the 8 K-slots of reduction step 2*kb + half).
-      u32x4 pk[NKC];
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p0 = fast_exp2(fmaf(s[kb][8 * half + 2 * i], c, -m));
-            const float p1 = fast_exp2(fmaf(s[kb][8 * half + 2 * i + 1], c, -m));
-            rs += p0 + p1;
-            pk[2 * kb + half][i] = T::pack2(p0, p1);
-          }
-      lpart += rs;
+      u32x4 pk[NKC];  // P^T, the B operand of O^T += V^T P^T
+      softmax_tile<T, NKB, NDB>(s, pk, m, lpart, oacc, c);
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
@@ -414,35 +430,7 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
     const int ts = j * BC;
     const bool need_mask = (ts + BC > Nk) || (CAUSAL && ts + BC - 1 > wq0 + dlt);
     if (need_mask) mask_tile<CAUSAL, NKB>(s, ts, Nk, myq + dlt, hh);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    const float mt = max_halves(mx) * c;
-    if (wave_any(mt > m + kRescaleSlack)) {
-      const float mnew = fmaxf(m, mt);
-      const float alpha = fast_exp2(m - mnew);
-      m = mnew;
-      lpart *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p0 = fast_exp2(fmaf(s[kb][8 * half + 2 * i], c, -m));
-          const float p1 = fast_exp2(fmaf(s[kb][8 * half + 2 * i + 1], c, -m));
-          rs += p0 + p1;
-          pk[2 * kb + half][i] = T::pack2(p0, p1);
-        }
-    lpart += rs;
+    softmax_tile<T, NKB, NDB>(s, pk, m, lpart, oacc, c);
   };
 
   // K of tile j+1 and V of tile j are loaded at slot 2j (two buffers each)
