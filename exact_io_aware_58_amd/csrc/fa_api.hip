@@ -128,10 +128,10 @@ extern "C" int fa_bwd(int dtype, int B, int H, int N, int D, float scale, int ca
   const size_t rows_bytes = delta_bytes(B, H, N);
   if (!workspace || workspace_bytes < 2 * rows_bytes) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
-  float* delta = (float*)workspace;
-  float* lse2 = (float*)((char*)workspace + rows_bytes);
+  float* ndelta = (float*)workspace;
+  float* nlse = (float*)((char*)workspace + rows_bytes);
   fa::BwdArgs a{dtype, B, H, N, D, scale, causal ? 1 : 0, Q, K, V, O, dO, LSE,
-                dQ, dK, dV, delta, lse2, (hipStream_t)stream};
+                dQ, dK, dV, ndelta, nlse, (hipStream_t)stream};
   hipError_t e;
   {
     fa::TimedLaunch t(FA_KERNEL_BWD_DELTA, a.stream);

@@ -17,8 +17,8 @@
 //   dS = P * (dP - Delta),  dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Three kernels, no atomics (bit-for-bit repeatable):
-//   1. delta: Delta_i = dO_i . O_i and LSE_i * log2(e), float32, into the
-//             caller's workspace.
+//   1. delta: -Delta_i = -dO_i . O_i and -LSE_i / scale, float32, into the
+//             caller's workspace (negated so they can seed accumulators).
 //   2. dkdv:  a workgroup keeps 128 key rows resident (each wave 32 keys, K and
 //             V as VGPR operands, dK^T and dV^T accumulators in VGPRs) and
 //             streams query tiles (Q, dO, LSE, Delta) into double-buffered LDS
@@ -26,7 +26,10 @@
 //             dP = dO V^T leave one key per lane, so P and dS feed straight in
 //             as B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A
 //             operands come from the same row-major Q and dO tiles through
-//             transposing LDS reads.
+//             transposing LDS reads.  The S and dP accumulators start at
+//             -LSE/scale and -Delta of their query rows instead of zero, so
+//             the MFMAs leave S - LSE/scale and dP - Delta: P is one multiply
+//             and an exp2, dS one multiply.
 //   3. dq:    a workgroup keeps 128 query rows resident (Q, dO as operands,
 //             LSE and Delta one scalar per lane) and streams key tiles (K, V).
 //             S^T = K Q^T and dP^T = V dO^T leave one query per lane, so dS^T
@@ -46,12 +49,12 @@ namespace fa {
 
 // ------------------------------------------------------------------ delta
 
-// Delta_i = dO_i . O_i (fp32) and LSE_i * log2(e), one row per D/8 lanes.
+// -Delta_i = -dO_i . O_i (fp32) and -LSE_i / scale, one row per D/8 lanes.
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 bwd_delta_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-                 const float* __restrict__ LSE, float* __restrict__ delta,
-                 float* __restrict__ lse2, size_t rows) {
+                 const float* __restrict__ LSE, float* __restrict__ ndelta,
+                 float* __restrict__ nlse, float inv_scale, size_t rows) {
   constexpr int TPR = D / 8;  // threads per row, 16 bytes each
   constexpr int RPB = 256 / TPR;
   const int part = threadIdx.x % TPR;
@@ -70,8 +73,8 @@ bwd_delta_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO
 #pragma unroll
     for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
     if (row < rows && part == 0) {
-      delta[row] = acc;
-      lse2[row] = LSE[row] * kLog2e;
+      ndelta[row] = -acc;
+      nlse[row] = -LSE[row] * inv_scale;
     }
   }
 }
@@ -97,13 +100,13 @@ template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, DkvTile<D>::MIN_WG)
 bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                const float* __restrict__ lse2, const float* __restrict__ delta,
+                const float* __restrict__ nlse, const float* __restrict__ ndelta,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, float c,
                 float scale, int nkt, int total) {
   constexpr int BR = DkvTile<D>::BR;
   constexpr int TILE = BR * D;                  // elements of one Q or dO tile
   constexpr int BLOCKS = TILE * 2 / 1024;       // 1 KiB blocks per tile
-  constexpr int STAGE = 2 * TILE + 2 * 64 * 2;  // Q, dO, then 64 LSE2 + 64 Delta floats
+  constexpr int STAGE = 2 * TILE + 2 * 64 * 2;  // Q, dO, then 64 -LSE/scale + 64 -Delta floats
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
   static_assert(BLOCKS == 8, "two blocks of Q and two of dO per wave");
@@ -129,8 +132,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const i32x4 rQ = rsrc_words(Q + base, head_bytes);  // direct-to-LDS sources
   const i32x4 rdO = rsrc_words(dO + base, head_bytes);
-  const i32x4 rL = rsrc_words(lse2 + (size_t)bh * N, (uint32_t)N * 4);
-  const i32x4 rD = rsrc_words(delta + (size_t)bh * N, (uint32_t)N * 4);
+  const i32x4 rL = rsrc_words(nlse + (size_t)bh * N, (uint32_t)N * 4);
+  const i32x4 rD = rsrc_words(ndelta + (size_t)bh * N, (uint32_t)N * 4);
   const auto rK = make_rsrc(K + base, head_bytes);
   const auto rV = make_rsrc(V + base, head_bytes);
 
@@ -161,8 +164,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int ntiles = qstart < N ? (N - qstart + BR - 1) / BR : 0;
 
   // Direct global->LDS loads of one query tile: each wave two blocks of Q and
-  // two of dO; wave 0 also 64 LSE2 values, wave 1 64 Delta values.  Rows
-  // past N arrive as zeros (then P = 1 but dO = Q = 0: no contribution).
+  // two of dO; wave 0 also 64 -LSE/scale values, wave 1 64 -Delta values.
+  // Rows past N arrive as zeros (then P = 1 but dO = Q = 0: no contribution).
   auto dma = [&](const uint16_t* S0, int qs) {
 #pragma unroll
     for (int i = 0; i < BLOCKS / 4; ++i) {
@@ -196,17 +199,27 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int NQB = BR / 32;
     const uint16_t* Qs = S0;
     const uint16_t* dOs = S0 + TILE;
-    const float* lse2s = reinterpret_cast<const float*>(S0 + 2 * TILE);
-    const float* dlts = lse2s + 64;
+    const float* nls = reinterpret_cast<const float*>(S0 + 2 * TILE);
+    const float* nds = nls + 64;
     // block qb holds queries that see some key of this wave
     auto live = [&](int qb) { return !MASKED || qs + qb * 32 + 31 >= wk0; };
+    // lane: key `mykey`; register r of block qb: query
+    // qs + 32qb + 8*(r/4) + 4*hh + r%4.  The accumulators start at that
+    // query's -LSE/scale (S) and -Delta (dP): four consecutive registers are
+    // four consecutive queries, one 16-byte LDS read each.
     f32x16 s[NQB], dp[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[qb][r] = 0.f;
-        dp[qb][r] = 0.f;
+      for (int g = 0; g < 4; ++g) {
+        const int qo = qb * 32 + 8 * g + 4 * hh;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(nls + qo);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(nds + qo);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[qb][4 * g + e] = l4[e];
+          dp[qb][4 * g + e] = d4[e];
+        }
       }
 #pragma unroll
     for (int cc = 0; cc < NDC; ++cc)
@@ -216,8 +229,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           s[qb] = T::mfma(ld_lds16(Qs + qb * 32 * D + roff[cc]), kf[cc], s[qb]);
           dp[qb] = T::mfma(ld_lds16(dOs + qb * 32 * D + roff[cc]), vf[cc], dp[qb]);
         }
-    // lane: key `mykey`; register r of block qb: query
-    // qs + 32qb + 8*(r/4) + 4*hh + r%4
+    // P = exp2(c (S - LSE/scale)), dS = P (dP - Delta)
     u32x4 pp[NQB][2], dsp[NQB][2];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -225,16 +237,14 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int qo = qb * 32 + 8 * g + 4 * hh;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qo);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlts + qo);
         float p[4], ds[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          float pv = fast_exp2(fmaf(s[qb][r], c, -l4[e]));
+          float pv = fast_exp2(s[qb][r] * c);
           if (need_mask && qs + qo + e < mykey) pv = 0.f;
           p[e] = pv;
-          ds[e] = pv * (dp[qb][r] - d4[e]);
+          ds[e] = pv * dp[qb][r];
         }
         pp[qb][g >> 1][2 * (g & 1)] = T::pack2(p[0], p[1]);
         pp[qb][g >> 1][2 * (g & 1) + 1] = T::pack2(p[2], p[3]);
@@ -324,7 +334,7 @@ template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-              const float* __restrict__ lse2g, const float* __restrict__ delta,
+              const float* __restrict__ nlse, const float* __restrict__ ndelta,
               uint16_t* __restrict__ dQ, int N, float c, float scale, int nqt, int total) {
   constexpr int BC = DqTile<D>::BC;
   constexpr int TILE = BC * D;             // elements of one K or V tile
@@ -365,10 +375,11 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     qf[cc] = buf_load16(rQ, off);
     gf[cc] = buf_load16(rdO, off);
   }
-  const auto rL = make_rsrc(lse2g + (size_t)bh * N, (uint32_t)N * 4);
-  const auto rD = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
-  const float lse2 = buf_load_f32(rL, (uint32_t)myq * 4u);
-  const float dlt = buf_load_f32(rD, (uint32_t)myq * 4u);
+  const auto rL = make_rsrc(nlse + (size_t)bh * N, (uint32_t)N * 4);
+  const auto rD = make_rsrc(ndelta + (size_t)bh * N, (uint32_t)N * 4);
+  // exponent c S - LSE log2(e) = c S + c (-LSE/scale)
+  const float lbias = c * buf_load_f32(rL, (uint32_t)myq * 4u);
+  const float ndlt = buf_load_f32(rD, (uint32_t)myq * 4u);  // -Delta
 
   int roff[NDC];
 #pragma unroll
@@ -436,12 +447,12 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int r = 8 * half + 2 * i + e;
-            float pv = fast_exp2(fmaf(s[kb][r], c, -lse2));
+            float pv = fast_exp2(fmaf(s[kb][r], c, lbias));
             if (need_mask) {
               const int key = ts + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
               if (key >= N || (CAUSAL && key > myq)) pv = 0.f;
             }
-            ds2[e] = pv * (dp[kb][r] - dlt);
+            ds2[e] = pv * (dp[kb][r] + ndlt);
           }
           dsk[2 * kb + half][i] = T::pack2(ds2[0], ds2[1]);
         }
@@ -509,10 +520,12 @@ static hipError_t delta16(const BwdArgs& a) {
   const unsigned grid = (unsigned)(blocks < (1u << 20) ? blocks : (1u << 20));
   if (a.D == 64)
     hipLaunchKernelGGL((bwd_delta_kernel<T, 64>), dim3(grid), dim3(256), 0, a.stream,
-                       (const uint16_t*)a.O, (const uint16_t*)a.dO, a.LSE, a.delta, a.lse2, rows);
+                       (const uint16_t*)a.O, (const uint16_t*)a.dO, a.LSE, a.ndelta, a.nlse,
+                       1.f / a.scale, rows);
   else
     hipLaunchKernelGGL((bwd_delta_kernel<T, 128>), dim3(grid), dim3(256), 0, a.stream,
-                       (const uint16_t*)a.O, (const uint16_t*)a.dO, a.LSE, a.delta, a.lse2, rows);
+                       (const uint16_t*)a.O, (const uint16_t*)a.dO, a.LSE, a.ndelta, a.nlse,
+                       1.f / a.scale, rows);
   return hipGetLastError();
 }
 
@@ -526,7 +539,7 @@ static hipError_t dkdv(const BwdArgs& a) {
   const int total = nkt * a.B * a.H;
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
                      (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                     (const uint16_t*)a.dO, a.lse2, a.delta, (uint16_t*)a.dK, (uint16_t*)a.dV,
+                     (const uint16_t*)a.dO, a.nlse, a.ndelta, (uint16_t*)a.dK, (uint16_t*)a.dV,
                      a.N, a.scale * kLog2e, a.scale, nkt, total);
   return hipGetLastError();
 }
@@ -547,7 +560,7 @@ static hipError_t dq(const BwdArgs& a) {
   const int total = nqt * a.B * a.H;
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
                      (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                     (const uint16_t*)a.dO, a.lse2, a.delta, (uint16_t*)a.dQ, a.N,
+                     (const uint16_t*)a.dO, a.nlse, a.ndelta, (uint16_t*)a.dQ, a.N,
                      a.scale * kLog2e, a.scale, nqt, total);
   return hipGetLastError();
 }

@@ -29,8 +29,8 @@ struct BwdArgs {
   const void *Q, *K, *V, *O, *dO;
   const float* LSE;
   void *dQ, *dK, *dV;
-  float* delta;  // [B, H, N] float32 in the caller's workspace: dO_i . O_i
-  float* lse2;   // [B, H, N] float32 in the caller's workspace: LSE_i * log2(e)
+  float* ndelta;  // [B, H, N] float32 in the caller's workspace: -dO_i . O_i
+  float* nlse;    // [B, H, N] float32 in the caller's workspace: -LSE_i / scale
   hipStream_t stream;
 };
 

@@ -121,8 +121,8 @@ int fa_merge(int dtype, int B, int H, int N, int D, void* O, float* LSE, const v
 
 /*
  * Bytes of device workspace fa_bwd needs for this problem: two float32
- * [B, H, N] arrays, each padded to 256 bytes -- the per-row Delta_i =
- * dO_i . O_i and LSE_i * log2(e).  Returns 0 for invalid or unsupported
+ * [B, H, N] arrays, each padded to 256 bytes -- the per-row -Delta_i =
+ * -dO_i . O_i and -LSE_i / scale.  Returns 0 for invalid or unsupported
  * problems (fp32 has no backward).
  */
 size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int D, int causal);
