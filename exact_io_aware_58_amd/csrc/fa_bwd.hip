@@ -34,6 +34,9 @@
 //             LSE and Delta one scalar per lane) and streams key tiles (K, V).
 //             S^T = K Q^T and dP^T = V dO^T leave one query per lane, so dS^T
 //             feeds dQ^T += K^T dS^T directly (K^T by transposing reads).
+//             Its S and dP accumulators start from register blocks holding
+//             the lane's -LSE/scale and -Delta (an MFMA's C and D operands
+//             may differ, so the seeds survive every tile).
 // The dq kernel recomputes S and dP a second time; that costs two extra
 // contractions per tile but removes every cross-workgroup reduction.
 #include <hip/hip_runtime.h>
@@ -377,9 +380,16 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
   const auto rL = make_rsrc(nlse + (size_t)bh * N, (uint32_t)N * 4);
   const auto rD = make_rsrc(ndelta + (size_t)bh * N, (uint32_t)N * 4);
-  // exponent c S - LSE log2(e) = c S + c (-LSE/scale)
-  const float lbias = c * buf_load_f32(rL, (uint32_t)myq * 4u);
+  // Seeds of the S and dP accumulators: every register of a lane holds the
+  // lane's query, so S starts at -LSE/scale and dP at -Delta in all 16.
+  const float nls = buf_load_f32(rL, (uint32_t)myq * 4u);
   const float ndlt = buf_load_f32(rD, (uint32_t)myq * 4u);  // -Delta
+  f32x16 seed_s, seed_dp;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    seed_s[r] = nls;
+    seed_dp[r] = ndlt;
+  }
 
   int roff[NDC];
 #pragma unroll
@@ -422,12 +432,10 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const bool need_mask = MASKED && ((ts + BC > N) || (CAUSAL && ts + BC - 1 > wq0));
     f32x16 s[NKB], dp[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[kb][r] = 0.f;
-        dp[kb][r] = 0.f;
-      }
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = seed_s;
+      dp[kb] = seed_dp;
+    }
 #pragma unroll
     for (int cc = 0; cc < NDC; ++cc)
 #pragma unroll
@@ -447,12 +455,12 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int r = 8 * half + 2 * i + e;
-            float pv = fast_exp2(fmaf(s[kb][r], c, lbias));
+            float pv = fast_exp2(s[kb][r] * c);
             if (need_mask) {
               const int key = ts + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
               if (key >= N || (CAUSAL && key > myq)) pv = 0.f;
             }
-            ds2[e] = pv * (dp[kb][r] + ndlt);
+            ds2[e] = pv * dp[kb][r];
           }
           dsk[2 * kb + half][i] = T::pack2(ds2[0], ds2[1]);
         }
