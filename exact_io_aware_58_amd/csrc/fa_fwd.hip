@@ -70,11 +70,19 @@ constexpr float kSumLimit = 65536.f;
 // lowest finite float) the wave takes the tile maximum, rescales O and l to
 // it -- exact, since O and l always share the reference -- and exponentiates
 // again.  The row maximum is therefore off the common path.
-template <typename T, int NKB, int NDB>
+//
+// SEED: the score accumulators started from the block `sd` holding -m/c in
+// every register (an MFMA's C operand need not be its destination, so the
+// block survives), i.e. s arrives as s - m/c and a weight costs a multiply
+// and an exp2.  Until the row has a reference (m still the lowest float) sd
+// is 0 and the wave takes the slow path, which also refreshes sd.
+template <typename T, int NKB, int NDB, bool SEED>
 __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[NKB], u32x4 (&pk)[2 * NKB],
                                              float& m, float& lpart, f32x16 (&oacc)[NDB],
-                                             float c) {
-  auto exp_pack = [&]() {
+                                             float c, f32x16& sd) {
+  // bias: added to c*s before the exp2 (unused on the seeded fast path)
+  auto exp_pack = [&](float bias, auto fast) {
+    constexpr bool FAST = decltype(fast)::value;
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -82,29 +90,38 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[NKB], u32x4 (&pk)
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p0 = fast_exp2(fmaf(s[kb][8 * half + 2 * i], c, -m));
-          const float p1 = fast_exp2(fmaf(s[kb][8 * half + 2 * i + 1], c, -m));
+          const float x0 = s[kb][8 * half + 2 * i], x1 = s[kb][8 * half + 2 * i + 1];
+          const float p0 = fast_exp2(FAST ? x0 * c : fmaf(x0, c, bias));
+          const float p1 = fast_exp2(FAST ? x1 * c : fmaf(x1, c, bias));
           rs += p0 + p1;
           pk[2 * kb + half][i] = T::pack2(p0, p1);
         }
     return rs;
   };
-  float rs = exp_pack();
-  if (wave_any(!(rs <= kSumLimit))) {
+  const bool fresh = m == -FLT_MAX;  // no reference yet (then sd = 0)
+  float rs = SEED ? exp_pack(0.f, std::true_type()) : exp_pack(-m, std::false_type());
+  if (wave_any(!(rs <= kSumLimit) || (SEED && fresh))) {
+    // the scores are c*s - meff in log2 units
+    const float meff = SEED ? (fresh ? 0.f : m) : 0.f;
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    const float mnew = fmaxf(m, max_halves(mx) * c);
+    const float mnew = fmaxf(m, fmaf(max_halves(mx), c, meff));
     const float alpha = fast_exp2(m - mnew);  // 0 on the first tile
-    m = mnew;
     lpart *= alpha;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    rs = exp_pack();
+    rs = exp_pack(meff - mnew, std::false_type());
+    m = mnew;
+    if constexpr (SEED) {
+      const float v = m == -FLT_MAX ? 0.f : -m / c;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sd[r] = v;
+    }
   }
   lpart += rs;
 }
@@ -228,6 +245,10 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // exp2(-inf) = 0 and rescale factors exp2(0) = 1 instead of NaN.
   float m = -FLT_MAX;
   float lpart = 0.f;
+  constexpr bool SEED = D == 64;  // registers allow the seed block at D = 64
+  f32x16 sd;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sd[r] = 0.f;
 
   // MASKED: ragged tail or causal-diagonal tile (per-wave skip, element
   // mask); the others run straight-line code.
@@ -238,9 +259,14 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       // S^T[key][q] for the wave's 32 queries and the tile's BC keys.
       f32x16 s[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb) {
+        if constexpr (SEED) {
+          s[kb] = sd;
+        } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+          for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        }
+      }
 #pragma unroll
       for (int cc = 0; cc < NDC; ++cc)
 #pragma unroll
@@ -249,7 +275,7 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       const bool need_mask = MASKED && ((ts + BC > Nk) || (CAUSAL && ts + BC - 1 > wq0 + dlt));
       if (need_mask) mask_tile<CAUSAL, NKB>(s, ts, Nk, myq + dlt, hh);
       u32x4 pk[NKC];  // P^T, the B operand of O^T += V^T P^T
-      softmax_tile<T, NKB, NDB>(s, pk, m, lpart, oacc, c);
+      softmax_tile<T, NKB, NDB, SEED>(s, pk, m, lpart, oacc, c, sd);
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
@@ -393,6 +419,10 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m = -FLT_MAX;  // reference max (log2 units), moved lazily; see fwd16_kernel
+  constexpr bool SEED = D == 64;
+  f32x16 sd;  // seed of the score accumulators (see softmax_tile)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sd[r] = 0.f;
   float lpart = 0.f;    // partial row sum over this lane's keys
   f32x16 s[NKB];        // scores of the tile between its M and X phases
   u32x4 pk[NKC];        // probabilities between X(j) and M(j+1)
@@ -414,9 +444,14 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
     }
     if (j < ntiles && active(j)) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb) {
+        if constexpr (SEED) {
+          s[kb] = sd;
+        } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+          for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        }
+      }
 #pragma unroll
       for (int cc = 0; cc < NDC; ++cc)
 #pragma unroll
@@ -430,7 +465,7 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
     const int ts = j * BC;
     const bool need_mask = (ts + BC > Nk) || (CAUSAL && ts + BC - 1 > wq0 + dlt);
     if (need_mask) mask_tile<CAUSAL, NKB>(s, ts, Nk, myq + dlt, hh);
-    softmax_tile<T, NKB, NDB>(s, pk, m, lpart, oacc, c);
+    softmax_tile<T, NKB, NDB, SEED>(s, pk, m, lpart, oacc, c, sd);
   };
 
   // K of tile j+1 and V of tile j are loaded at slot 2j (two buffers each)
