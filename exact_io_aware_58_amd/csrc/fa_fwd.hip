@@ -16,23 +16,30 @@
 // output is scaled by exp(m_old - m_new), and the output is divided by l once
 // after the last tile.  Scores and probabilities exist only in registers.
 //
-// 16-bit kernel, gfx950 design (one workgroup = 4 waves = 128 query rows):
+// 16-bit kernels, gfx950 design (fwd16_kernel: 4 waves, 128 query rows per
+// workgroup; fwd16pp_kernel: 8 waves, 256 rows, described at its definition):
 //   * each wave owns 32 query rows; its Q fragments stay in VGPRs for the
 //     whole key loop (loaded once from HBM);
-//   * key/value tiles are double-buffered in LDS: K row-major, V transposed
-//     (d-major) so both MFMA operands are single 16-byte LDS reads; rows are
-//     padded by 16 bytes so the 32 rows a wave reads land in distinct banks;
+//   * K and V tiles are double-buffered in LDS, row-major with their 16-byte
+//     chunks swizzled per row, and filled by direct global->LDS loads issued
+//     a tile ahead; K fragments are 16-byte LDS reads, V^T fragments come
+//     from the row-major V tile through transposing LDS reads; neither access
+//     has bank conflicts;
 //   * the score tile is computed transposed, S^T = K Q^T, so each lane holds
 //     one query row: the row max needs one exchange between wave halves, the
 //     row sum none until the epilogue, and the O^T accumulators of a lane all
 //     belong to its row, so the rescale is a per-lane multiply;
 //   * P^T leaves the S^T accumulators already in the B-operand layout of
-//     O^T += V^T P^T; the K-slot order this implies is folded into the order
-//     in which V^T columns are stored;
-//   * exp is exp2 with scale*log2(e) folded into one FMA per score;
+//     O^T += V^T P^T, and the transposing reads hand each lane exactly the
+//     keys its P registers hold;
+//   * exp is exp2 with scale*log2(e) folded into the score (one FMA, or at
+//     D = 64 one multiply on accumulators seeded with the reference), and
+//     the reference maximum moves lazily (see softmax_tile);
 //   * causal: tiles wholly above a wave's rows are skipped per wave, the
 //     workgroup stops at its last visible tile, only diagonal/tail tiles pay
-//     for the mask, and the longest query blocks are launched first.
+//     for the mask, and the longest query blocks are launched first;
+//   * an optional offset between query and key positions (partial attention
+//     over blocks of a longer sequence) shifts all of these by a constant.
 #include <hip/hip_runtime.h>
 
 #include <float.h>
