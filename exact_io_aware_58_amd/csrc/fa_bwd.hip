@@ -148,6 +148,11 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     kf[cc] = buf_load16(rK, off);
     vf[cc] = buf_load16(rV, off);
   }
+#pragma unroll
+  for (int cc = 0; cc < NDC; ++cc) {
+    settle(kf[cc]);
+    settle(vf[cc]);
+  }
 
   // Per-lane LDS offsets.  Row-major operands (S and dP): query row l32 of a
   // 32-row block, columns 16cc + 8hh.  Transposed operands (Q^T, dO^T for
@@ -378,12 +383,19 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     qf[cc] = buf_load16(rQ, off);
     gf[cc] = buf_load16(rdO, off);
   }
+#pragma unroll
+  for (int cc = 0; cc < NDC; ++cc) {
+    settle(qf[cc]);
+    settle(gf[cc]);
+  }
   const auto rL = make_rsrc(nlse + (size_t)bh * N, (uint32_t)N * 4);
   const auto rD = make_rsrc(ndelta + (size_t)bh * N, (uint32_t)N * 4);
   // Seeds of the S and dP accumulators: every register of a lane holds the
   // lane's query, so S starts at -LSE/scale and dP at -Delta in all 16.
   const float nls = buf_load_f32(rL, (uint32_t)myq * 4u);
   const float ndlt = buf_load_f32(rD, (uint32_t)myq * 4u);  // -Delta
+  settle(nls);
+  settle(ndlt);
   f32x16 seed_s, seed_dp;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {

@@ -81,6 +81,17 @@ __device__ inline float sum_halves(float x) {
 // zero, which only drops softmax weights smaller than 1e-38 of the row max.
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Makes the wave wait here until `v` has arrived.  For operands loaded once
+// before a loop: left alone, the compiler may issue such loads after the
+// prologue's barrier, and then waits on the memory counter inside the loop,
+// where the count also covers the direct-to-LDS prefetches in flight -- every
+// tile would stall until its prefetch landed.  The empty asm consumes the
+// value, so the wait happens once, here.
+template <typename V>
+__device__ __forceinline__ void settle(const V& v) {
+  asm volatile("" ::"v"(v));
+}
+
 // True on every lane when any lane of the wave has `pred` set.
 __device__ inline bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 

@@ -206,6 +206,8 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   u32x4 qf[NDC];
 #pragma unroll
   for (int cc = 0; cc < NDC; ++cc) qf[cc] = buf_load16(rQ, ((uint32_t)myq * D + 16 * cc + 8 * hh) * 2u);
+#pragma unroll
+  for (int cc = 0; cc < NDC; ++cc) settle(qf[cc]);
 
   // Per-lane LDS offsets (elements).  K operand: row l32 of a 32-key block,
   // columns 16cc + 8hh.  V^T operand via transposing reads: for d-block db
@@ -396,6 +398,8 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
 #pragma unroll
   for (int cc = 0; cc < NDC; ++cc)
     qf[cc] = buf_load16(rQ, ((uint32_t)myq * D + 16 * cc + 8 * hh) * 2u);
+#pragma unroll
+  for (int cc = 0; cc < NDC; ++cc) settle(qf[cc]);
 
   // LDS offsets as in fwd16_kernel.
   int koff[NDC];
