@@ -484,6 +484,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const u32x4 a = cat(ld_lds_tr(kb16 + toffs[db][0]), ld_lds_tr(kb16 + toffs[db][1]));
         acc[db] = T::mfma(a, dsk[kc], acc[db]);
       }
+    // two accumulator chains: keep the K^T reads three MFMAs ahead
+    if constexpr (!MASKED) pipeline_reads<NKC * NDB, 2, 3, 1>();
   };
 
   // Tiles wholly visible to every row of the workgroup (no tail, not past

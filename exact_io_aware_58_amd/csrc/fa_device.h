@@ -258,6 +258,24 @@ __device__ inline u32x2 ld_lds_tr(const uint16_t* p) {
 }
 __device__ inline u32x4 cat(u32x2 lo, u32x2 hi) { return u32x4{lo[0], lo[1], hi[0], hi[1]}; }
 
+// ---- instruction scheduling ----
+// Scheduling hint for a block of NM MFMAs that each consume R LDS reads:
+// issue the reads of the first AHEAD MFMAs, then alternate one MFMA with the
+// reads of the MFMA AHEAD places later.  Left to itself the compiler issues
+// each read just before its MFMA; where only two or four accumulator chains
+// are in flight every MFMA then waits for LDS latency.
+template <int NM, int R, int AHEAD, int GROUP_ID>
+__device__ __forceinline__ void pipeline_reads() {
+  constexpr int kDsRead = 0x100, kMfma = 0x008;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, R * AHEAD, GROUP_ID);
+#pragma unroll
+  for (int i = 0; i < NM - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, GROUP_ID);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, R, GROUP_ID);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD, GROUP_ID);
+}
+
 // ---- workgroup order ----
 // Workgroups are dealt round-robin to the 8 XCDs (blockIdx.x % 8).  Remap so
 // that each XCD receives one contiguous range of logical tiles: tiles of the

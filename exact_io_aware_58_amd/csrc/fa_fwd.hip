@@ -357,23 +357,6 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // phases before they are read (K of tile j+1 and V of tile j at phase 2j).
 constexpr int kPpBR = 256;
 
-// Scheduling hint for a block of NM MFMAs that each consume R LDS reads:
-// issue the reads of the first AHEAD MFMAs, then alternate one MFMA with the
-// reads of the MFMA AHEAD places later.  Left to itself the compiler issues
-// each read just before its MFMA, and at D = 128 (two or four accumulator
-// chains) every MFMA then waits for LDS latency (c4 forward 6% slower).
-template <int NM, int R, int AHEAD, int GROUP_ID>
-__device__ __forceinline__ void pipeline_reads() {
-  constexpr int kDsRead = 0x100, kMfma = 0x008;
-  __builtin_amdgcn_sched_group_barrier(kDsRead, R * AHEAD, GROUP_ID);
-#pragma unroll
-  for (int i = 0; i < NM - AHEAD; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kMfma, 1, GROUP_ID);
-    __builtin_amdgcn_sched_group_barrier(kDsRead, R, GROUP_ID);
-  }
-  __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD, GROUP_ID);
-}
-
 template <typename T, int D, bool CAUSAL, int GROUP>
 __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
                                              const uint16_t* __restrict__ K,
