@@ -64,8 +64,10 @@ struct FwdTile<128> {
 };
 
 constexpr int kFwdBR = 128;  // query rows per workgroup (4 waves x 32)
-// Bound on a lane's partial row sum over one tile; it bounds every weight.
-constexpr float kSumLimit = 65536.f;
+// Bound on a lane's partial row sum over one tile; it bounds every weight,
+// and 2^15 keeps each weight finite when packed to fp16 (largest finite
+// value 65504: a weight just under 2^16 would round to +inf).
+constexpr float kSumLimit = 32768.f;
 
 // Online softmax of one tile.  Exponentiates the scores against the
 // reference maximum m (log2 units) and packs them as the B operand of

@@ -66,6 +66,41 @@ def test_forward_many_heads(N, causal, D, dtype):
     assert eo <= tol["o"] and el <= tol["lse"]
 
 
+@pytest.mark.parametrize("heads", [1, 512], ids=["4wave", "pingpong"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp16_weight_near_the_rescale_bound(causal, D, heads):
+    """The forward keeps a row's reference maximum until some lane's tile
+    sum passes a bound, so one weight can come close to that bound before a
+    rescale.  Built case: every query is a*e0, keys 0..127 are zero (the
+    reference settles at score 0 on the first tile), key 128 is b*e0 with
+    a*b = 16 - 2^-14 and scale = ln 2, i.e. its weight against that
+    reference is 2^15.99994 = 65533; every later key scores -30.  That
+    weight does not fit fp16 (largest finite 65504); packed as the PV
+    operand it would become +inf.  O must stay finite and match the oracle."""
+    say(f"[fwd-f16-bound] D={D} causal={causal} heads={heads}")
+    N = 300
+    a, b = 1.0 + 2.0 / 1024, 16.0 - 2.0 / 64  # both exact in fp16; a*b exact in fp32
+    q = np.zeros((1, heads, N, D), np.float16)
+    k = np.zeros((1, heads, N, D), np.float16)
+    q[..., 0] = a
+    k[:, :, 128, 0] = b
+    k[:, :, 129:, 0] = -30.0
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal((1, heads, N, D)).astype(np.float16)
+    devs = {n: torch.from_numpy(x).cuda() for n, x in (("q", q), ("k", k), ("v", v))}
+    scale = float(np.log(2.0))
+    o, lse = _fwd(devs, scale, causal)
+    got_o, got_l = to_f64(o), to_f64(lse)
+    assert np.isfinite(got_o).all() and np.isfinite(got_l).all()
+    h = [0, heads - 1]  # identical heads: check the first and the last
+    ro, rl = oracle.attention_fwd(q[:, h].astype(np.float64), k[:, h].astype(np.float64),
+                                  v[:, h].astype(np.float64), scale, causal)
+    eo, el = max_abs(got_o[:, h], ro), max_abs(got_l[:, h], rl)
+    say(f"    max abs O={eo:.2e} LSE={el:.2e}")
+    assert eo <= TOL["f16"]["o"] and el <= TOL["f16"]["lse"]
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
