@@ -15,6 +15,8 @@ constexpr int kMaxN = 1 << 23;  // one head's tensor stays below 4 GiB (buffer r
 // tensors far beyond one GPU's memory before that).
 constexpr double kMaxRows = 1073741824.0;  // 2^30
 constexpr long long kMaxPos = 1LL << 62;    // partial attention positions
+constexpr float kMinScale = 0x1p-32f;        // accepted softmax scales
+constexpr float kMaxScale = 0x1p32f;
 
 bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -24,7 +26,9 @@ int check_problem(int dtype, int B, int H, int N, int D, float scale) {
   if (B <= 0 || H <= 0 || N <= 0 || N > kMaxN) return FA_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
   if ((double)B * H * N > kMaxRows) return FA_ERR_INVALID_ARG;
-  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+  // scale * log2(e) is folded into one fp32 factor and divided back out of
+  // the seeded accumulators: keep it a normal number with room either side.
+  if (!(scale >= kMinScale && scale <= kMaxScale)) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }
 

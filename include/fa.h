@@ -25,8 +25,10 @@
  *     launched and no output is touched.
  *   - causal != 0 keeps key j for query i iff j <= i (diagonal included).
  *     The pages do not define the mask; this is the usual autoregressive one.
- *   - scale multiplies Q K^T before the softmax; it must be finite and > 0
- *     (the pages use 1/sqrt(D): [ijyty] naive_attention snippet).
+ *   - scale multiplies Q K^T before the softmax; it must lie in
+ *     [2^-32, 2^32] (NaN rejected).  The pages use 1/sqrt(D) ([ijyty]
+ *     naive_attention snippet); the range keeps scale * log2(e), which the
+ *     kernels fold into one fp32 factor, a normal number.
  *   - Entry points are stateless and may be called from several host threads
  *     (the optional kernel timer below is guarded by a mutex).
  */

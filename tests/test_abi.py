@@ -69,6 +69,9 @@ def test_version_and_status_strings(fa):
     (dict(scale=-0.125), -1),
     (dict(scale=float("inf")), -1),
     (dict(scale=float("nan")), -1),
+    (dict(scale=2.0 ** -33), -1),  # scale * log2(e) must stay a normal fp32
+    (dict(scale=2.0 ** 33), -1),
+    (dict(scale=1e-45), -1),       # fp32 denormal
 ])
 def test_fwd_rejects_bad_problem(fa, args, status):
     kw = dict(dtype=fa.FA_BF16, B=1, H=2, N=128, D=64, scale=0.125)
@@ -93,14 +96,14 @@ def test_workspace_bytes(fa):
     assert fa.fa_bwd_workspace_bytes(fa.FA_F32, 1, 1, 128, 64, 0) == 0
 
 
-def _bwd(fa, dtype=None, ws_bytes=None, ws=P[10], ptr_over=None, D=64, N=128):
+def _bwd(fa, dtype=None, ws_bytes=None, ws=P[10], ptr_over=None, D=64, N=128, scale=0.125):
     dtype = fa.FA_BF16 if dtype is None else dtype
     ptrs = P[:9]
     if ptr_over:
         ptrs[ptr_over[0]] = ptr_over[1]
     if ws_bytes is None:
         ws_bytes = fa.fa_bwd_workspace_bytes(fa.FA_BF16, 1, 2, N, 64, 0)
-    return fa.fa_bwd(dtype, 1, 2, N, D, 0.125, 0, *ptrs, ws, ws_bytes, None)
+    return fa.fa_bwd(dtype, 1, 2, N, D, scale, 0, *ptrs, ws, ws_bytes, None)
 
 
 def test_bwd_validation(fa):
@@ -109,6 +112,8 @@ def test_bwd_validation(fa):
     assert _bwd(fa, ws=A + 4) == fa.FA_ERR_INVALID_ARG
     assert _bwd(fa, dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
     assert _bwd(fa, D=80) == fa.FA_ERR_UNSUPPORTED
+    for bad in (0.0, 2.0 ** -33, 2.0 ** 33, float("nan")):
+        assert _bwd(fa, scale=bad) == fa.FA_ERR_INVALID_ARG
     for i in range(9):
         assert _bwd(fa, ptr_over=(i, 0)) == fa.FA_ERR_INVALID_ARG
         assert _bwd(fa, ptr_over=(i, A + 2)) == fa.FA_ERR_INVALID_ARG
@@ -136,6 +141,7 @@ def test_timing_read_bounds(fa):
     (dict(k_pos=(1 << 62) + 1), -1),
     (dict(scale=0.0), -1),
     (dict(scale=float("nan")), -1),
+    (dict(scale=2.0 ** -40), -1),
 ])
 def test_fwd_partial_rejects_bad_problem(fa, args, status):
     kw = dict(dtype=fa.FA_BF16, Nq=100, Nk=300, D=64, scale=0.125, q_pos=0, k_pos=0)
