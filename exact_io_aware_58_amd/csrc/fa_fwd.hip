@@ -32,9 +32,10 @@
 //   * P^T leaves the S^T accumulators already in the B-operand layout of
 //     O^T += V^T P^T, and the transposing reads hand each lane exactly the
 //     keys its P registers hold;
-//   * exp is exp2 with scale*log2(e) folded into the score (one FMA, or at
-//     D = 64 one multiply on accumulators seeded with the reference), and
-//     the reference maximum moves lazily (see softmax_tile);
+//   * exp is exp2 with scale*log2(e) folded into the score: the score
+//     accumulators start from a register block holding the reference, so a
+//     weight is one multiply and one exp2; the reference maximum moves
+//     lazily (see softmax_tile);
 //   * causal: tiles wholly above a wave's rows are skipped per wave, the
 //     workgroup stops at its last visible tile, only diagonal/tail tiles pay
 //     for the mask, and the longest query blocks are launched first;
@@ -92,7 +93,7 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[NKB], u32x4 (&pk)
   // bias: added to c*s before the exp2 (unused on the seeded fast path)
   auto exp_pack = [&](float bias, auto fast) {
     constexpr bool FAST = decltype(fast)::value;
-    float rs = 0.f;
+    float rs = -0.f;  // -0 + x == x for every x, so the first add folds away
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -256,7 +257,7 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // exp2(-inf) = 0 and rescale factors exp2(0) = 1 instead of NaN.
   float m = -FLT_MAX;
   float lpart = 0.f;
-  constexpr bool SEED = D == 64;  // registers allow the seed block at D = 64
+  constexpr bool SEED = true;  // seeded score accumulators (see softmax_tile)
   f32x16 sd;
 #pragma unroll
   for (int r = 0; r < 16; ++r) sd[r] = 0.f;
@@ -283,6 +284,7 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
           s[kb] = T::mfma(ld_lds16(Ks + kb * 32 * D + koff[cc]), qf[cc], s[kb]);
+      if constexpr (D == 128) pipeline_reads<NDC * NKB, 1, 6, 0>();
       const bool need_mask = MASKED && ((ts + BC > Nk) || (CAUSAL && ts + BC - 1 > wq0 + dlt));
       if (need_mask) mask_tile<CAUSAL, NKB>(s, ts, Nk, myq + dlt, hh);
       u32x4 pk[NKC];  // P^T, the B operand of O^T += V^T P^T
@@ -295,6 +297,7 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           const u32x4 a = cat(ld_lds_tr(vb + voff[db][0]), ld_lds_tr(vb + voff[db][1]));
           oacc[db] = T::mfma(a, pk[kc], oacc[db]);
         }
+      if constexpr (D == 128) pipeline_reads<NKC * NDB, 2, 4, 1>();
     }
   };
 
@@ -358,6 +361,7 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // have two LDS buffers each, filled by direct global->LDS loads issued two
 // phases before they are read (K of tile j+1 and V of tile j at phase 2j).
 constexpr int kPpBR = 256;
+constexpr int kCUs = 256;  // compute units of an MI355X
 
 template <typename T, int D, bool CAUSAL, int GROUP>
 __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
@@ -432,7 +436,7 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m = -FLT_MAX;  // reference max (log2 units), moved lazily; see fwd16_kernel
-  constexpr bool SEED = D == 64;
+  constexpr bool SEED = true;
   f32x16 sd;  // seed of the score accumulators (see softmax_tile)
 #pragma unroll
   for (int r = 0; r < 16; ++r) sd[r] = 0.f;
@@ -454,7 +458,7 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
           const u32x4 a = cat(ld_lds_tr(vb + voff[db][0]), ld_lds_tr(vb + voff[db][1]));
           oacc[db] = T::mfma(a, pk[kc], oacc[db]);
         }
-      if constexpr (D == 128) pipeline_reads<NKC * NDB, 2, 4, 1>();
+      if constexpr (D == 128) pipeline_reads<NKC * NDB, 2, 3, 1>();
     }
     if (j < ntiles && active(j)) {
 #pragma unroll
@@ -471,7 +475,7 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
           s[kb] = T::mfma(ld_lds16(Kcur + kb * 32 * D + koff[cc]), qf[cc], s[kb]);
-      if constexpr (D == 128) pipeline_reads<NDC * NKB, 1, 6, 0>();
+      if constexpr (D == 128) pipeline_reads<NDC * NKB, 1, 4, 0>();
     }
   };
 
@@ -634,9 +638,13 @@ fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch16(const FwdArgs& a) {
-  // Enough 256-row workgroups to give every CU at least two: ping-pong kernel.
+  // Ping-pong kernel (one 256-row workgroup per CU at a time) when its grid
+  // gives every CU at least two workgroups, or fills whole rounds of one per
+  // CU; other grids run the 4-wave kernel, two 128-row workgroups per CU,
+  // whose finer granularity evens out a partial last round.
   const int npp = (a.Nq + kPpBR - 1) / kPpBR;
-  if ((long)npp * a.B * a.H >= 512) {
+  const long wpp = (long)npp * a.B * a.H;
+  if (wpp >= 2 * kCUs || wpp % kCUs == 0) {
     const int total = npp * a.B * a.H;
     hipLaunchKernelGGL((fwd16pp_kernel<T, D, CAUSAL>), dim3(total), dim3(512), 0, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,

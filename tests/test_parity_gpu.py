@@ -66,6 +66,22 @@ def test_forward_many_heads(N, causal, D, dtype):
     assert eo <= tol["o"] and el <= tol["lse"]
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_one_round_of_pingpong(causal, D):
+    """A grid of exactly one 256-row workgroup per CU (128 heads x 2 query
+    blocks) also takes the ping-pong kernel; N = 300 leaves a ragged tail."""
+    say(f"[fwd-one-round] D={D} causal={causal}")
+    shape = (1, 128, 300, D)
+    vals, devs = draw_case(500 + D, shape, "bf16")
+    scale = 1.0 / np.sqrt(D)
+    o, lse = _fwd(devs, scale, causal)
+    ro, rl = oracle.attention_fwd(vals["q"], vals["k"], vals["v"], scale, causal)
+    eo, el = max_abs(to_f64(o), ro), max_abs(to_f64(lse), rl)
+    say(f"    max abs O={eo:.2e} LSE={el:.2e}")
+    assert eo <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"]
+
+
 @pytest.mark.parametrize("heads", [1, 512], ids=["4wave", "pingpong"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
