@@ -136,6 +136,27 @@ def test_backward_small(N, causal, D, dtype):
     assert eq <= tol and ek <= tol and ev <= tol
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 128, 300, 64), (2, 256, 257, 64)],
+                         ids=["128heads", "512heads"])
+def test_backward_many_heads(shape, causal, dtype):
+    """Grids of hundreds of heads (one or more full rounds of workgroups on
+    every CU) with ragged N: the last query block and key tile are partial in
+    every head; every element of dQ, dK, dV."""
+    say(f"[bwd-many-heads] shape={shape} causal={causal} dtype={dtype}")
+    vals, devs = draw_case(700 + shape[2], shape, dtype, grad=True)
+    scale = 1.0 / np.sqrt(shape[3])
+    o, lse = _fwd(devs, scale, causal)
+    dq, dk, dv = fa.backward(devs["q"], devs["k"], devs["v"], o, devs["do"], lse, scale, causal)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_bwd(vals["q"], vals["k"], vals["v"], vals["do"], scale, causal)
+    tol = TOL[dtype]["grad_rel"]
+    eq, ek, ev = rel_to_max(to_f64(dq), rq), rel_to_max(to_f64(dk), rk), rel_to_max(to_f64(dv), rv)
+    say(f"    rel-to-max dQ={eq:.2e} dK={ek:.2e} dV={ev:.2e}")
+    assert eq <= tol and ek <= tol and ev <= tol
+
+
 def test_output_rounding_is_nearest_even():
     """N = 2 with identical keys gives weights of exactly 1/2, so O is the
     exact fp32 mean of two bf16 values; pick means that sit exactly halfway
