@@ -384,9 +384,11 @@ def main():
     ap.add_argument("--sweep", default="",
                     help="comma-separated sequence lengths: print one JSON line per N "
                          "comparing with the three-kernel PyTorch path instead of the bench line")
+    ap.add_argument("--sweep-d", type=int, default=64, choices=(64, 128),
+                    help="head dimension of the --sweep runs (B=1, H=16)")
     args = ap.parse_args()
     if args.sweep:
-        run_sweep([int(x) for x in args.sweep.split(",")])
+        run_sweep([int(x) for x in args.sweep.split(",")], D=args.sweep_d)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
