@@ -157,6 +157,44 @@ def test_backward_many_heads(shape, causal, dtype):
     assert eq <= tol and ek <= tol and ev <= tol
 
 
+def test_timing_hooks_count_and_bound_the_launches():
+    """The per-kernel timing the bench reports: with timing on, every launch
+    is counted under its kernel, each duration is positive, and the summed
+    kernel times fit inside the wall time of the same launches (events on
+    the same stream around all of them)."""
+    say("[timing] B=1 H=16 N=2048 D=64 causal, 3 fwd+bwd")
+    shape = (1, 16, 2048, 64)
+    vals, devs = draw_case(41, shape, "bf16", grad=True)
+    scale = 1.0 / np.sqrt(64)
+    o, lse = _fwd(devs, scale, True)
+    dq, dk, dv = fa.backward(devs["q"], devs["k"], devs["v"], o, devs["do"], lse, scale, True)
+    torch.cuda.synchronize()
+    assert fa.fa_timing_enable(True) == fa.FA_OK
+    try:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            fa.forward(devs["q"], devs["k"], devs["v"], scale, True, out=o, lse=lse)
+            fa.backward(devs["q"], devs["k"], devs["v"], o, devs["do"], lse, scale, True,
+                        dq=dq, dk=dk, dv=dv)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = e0.elapsed_time(e1)
+        total = 0.0
+        for kid in (fa.FA_KERNEL_FWD, fa.FA_KERNEL_BWD_DELTA, fa.FA_KERNEL_BWD_DKDV,
+                    fa.FA_KERNEL_BWD_DQ):
+            n, ms, dropped = fa.fa_timing_read(kid)
+            say(f"    {fa.fa_kernel_name(kid)}: {n} launches, {ms:.4f} ms")
+            assert n == 3 and dropped == 0 and ms > 0.0
+            total += ms
+        n, ms, _ = fa.fa_timing_read(fa.FA_KERNEL_MERGE)
+        assert n == 0 and ms == 0.0
+        say(f"    kernels {total:.4f} ms within {wall:.4f} ms of wall time")
+        assert total <= wall * 1.02
+    finally:
+        fa.fa_timing_enable(False)
+
+
 def test_output_rounding_is_nearest_even():
     """N = 2 with identical keys gives weights of exactly 1/2, so O is the
     exact fp32 mean of two bf16 values; pick means that sit exactly halfway
