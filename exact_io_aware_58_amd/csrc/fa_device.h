@@ -135,12 +135,6 @@ __device__ inline void st_global8(void* p, u32x2 v) {
 __device__ inline u32x4 ld_lds16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
-__device__ inline void st_lds16(uint16_t* p, u32x4 v) {
-  *reinterpret_cast<u32x4*>(p) = v;
-}
-__device__ inline void st_lds8(uint16_t* p, u32x2 v) {
-  *reinterpret_cast<u32x2*>(p) = v;
-}
 
 // Select the 16-bit element j (0..7) of a 16-byte vector.
 __device__ inline uint32_t elem16(u32x4 v, int j) {
