@@ -11,9 +11,12 @@
 namespace {
 
 constexpr int kMaxN = 1 << 23;  // one head's tensor stays below 4 GiB (buffer range)
-// B*H*N rows at most: every grid stays below 2^32 work-items (and the
-// tensors far beyond one GPU's memory before that).
-constexpr double kMaxRows = 1073741824.0;  // 2^30
+constexpr double kMaxRows = 1073741824.0;  // B*H*N rows at most (2^30)
+// Grids are padded per head: the largest is the 8-wave forward's
+// B*H*ceil(N/256) workgroups of 512 work-items, at most
+// B*H*ceil(N/64) * 512.  Keeping B*H*ceil(N/64) below 2^23 keeps every
+// launch below 2^32 work-items (and every workgroup count an int).
+constexpr double kMaxPaddedBlocks = 8388608.0;  // 2^23
 constexpr long long kMaxPos = 1LL << 62;    // partial attention positions
 constexpr float kMinScale = 0x1p-32f;        // accepted softmax scales
 constexpr float kMaxScale = 0x1p32f;
@@ -26,6 +29,7 @@ int check_problem(int dtype, int B, int H, int N, int D, float scale) {
   if (B <= 0 || H <= 0 || N <= 0 || N > kMaxN) return FA_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
   if ((double)B * H * N > kMaxRows) return FA_ERR_INVALID_ARG;
+  if ((double)B * H * ((N + 63) / 64) >= kMaxPaddedBlocks) return FA_ERR_INVALID_ARG;
   // scale * log2(e) is folded into one fp32 factor and divided back out of
   // the seeded accumulators: keep it a normal number with room either side.
   if (!(scale >= kMinScale && scale <= kMaxScale)) return FA_ERR_INVALID_ARG;

@@ -22,7 +22,8 @@ struct Timer {
   std::mutex mu;
   bool on = false;
   std::vector<hipEvent_t> start, stop;
-  int next = 0;
+  int next = 0;      // next unused event slot
+  int in_flight = 0;  // slots taken by launches whose stop event is not yet recorded
   std::vector<Pending> pending;
   long long launches[FA_KERNEL_COUNT] = {};
   double total_ms[FA_KERNEL_COUNT] = {};
@@ -44,7 +45,9 @@ int drain(Timer& t) {
     t.total_ms[p.id] += ms;
   }
   t.pending.clear();
-  t.next = 0;
+  // Slots are reused only when no launch still holds one between its two
+  // events (another thread may be inside a timed launch).
+  if (t.in_flight == 0) t.next = 0;
   return FA_OK;
 }
 
@@ -59,13 +62,17 @@ TimedLaunch::TimedLaunch(int kernel_id, hipStream_t s) : id(kernel_id), stream(s
     return;
   }
   slot = t.next++;
-  if (hipEventRecord(t.start[slot], stream) != hipSuccess) slot = -1;
+  if (hipEventRecord(t.start[slot], stream) != hipSuccess)
+    slot = -1;
+  else
+    t.in_flight += 1;
 }
 
 TimedLaunch::~TimedLaunch() {
   if (slot < 0) return;
   Timer& t = timer();
   std::lock_guard<std::mutex> g(t.mu);
+  t.in_flight -= 1;
   if (hipEventRecord(t.stop[slot], stream) == hipSuccess) t.pending.push_back({id, slot});
 }
 

@@ -123,15 +123,33 @@ def _dtype_code(t):
 
 
 def _check_qkv(*ts):
-    shape, dtype = ts[0].shape, ts[0].dtype
+    shape, dtype, dev = ts[0].shape, ts[0].dtype, ts[0].device
     for t in ts:
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("tensors must be contiguous device tensors")
-        if t.shape != shape or t.dtype != dtype:
-            raise ValueError("tensors must share one (B, H, N, D) shape and dtype")
+        if t.shape != shape or t.dtype != dtype or t.device != dev:
+            raise ValueError("tensors must share one (B, H, N, D) shape, dtype and device")
     if len(shape) != 4:
         raise ValueError("expected (B, H, N, D) tensors")
     return shape
+
+
+def _check_out(t, like, name):
+    """A caller-supplied output must be a contiguous device tensor of the
+    input's shape and dtype on the same device (the kernels write every
+    element of it)."""
+    if (not t.is_cuda or not t.is_contiguous() or t.shape != like.shape
+            or t.dtype != like.dtype or t.device != like.device):
+        raise ValueError(f"{name} must be a contiguous {tuple(like.shape)} {like.dtype} tensor "
+                         f"on {like.device}")
+
+
+def _check_lse(t, B, H, N, like, name="lse"):
+    import torch
+    if (not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != (B, H, N)
+            or t.dtype != torch.float32 or t.device != like.device):
+        raise ValueError(f"{name} must be a contiguous float32 ({B}, {H}, {N}) tensor on "
+                         f"{like.device}")
 
 
 def _stream():
@@ -145,8 +163,10 @@ def forward(q, k, v, scale, causal=False, out=None, lse=None):
     B, H, N, D = _check_qkv(q, k, v)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, q, "out")
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_lse(lse, B, H, N, q)
     rc = fa_fwd(_dtype_code(q), B, H, N, D, float(scale), causal, q.data_ptr(), k.data_ptr(),
                 v.data_ptr(), out.data_ptr(), lse.data_ptr(), _stream())
     if rc != FA_OK:
@@ -166,10 +186,14 @@ def forward_partial(q, k, v, scale, causal=False, q_pos=0, k_pos=0, out=None, ls
     if (not q.is_cuda or not q.is_contiguous() or q.dtype != k.dtype
             or tuple(k.shape) != (B, H, Nk, D)):
         raise ValueError("q must be a contiguous (B, H, Nq, D) device tensor matching k, v")
+    if k.device != q.device:
+        raise ValueError("q, k, v must be on one device")
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, q, "out")
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_lse(lse, B, H, Nq, q)
     rc = fa_fwd_partial(_dtype_code(q), B, H, Nq, Nk, D, float(scale), causal, int(q_pos),
                         int(k_pos), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                         lse.data_ptr(), _stream())
@@ -180,13 +204,10 @@ def forward_partial(q, k, v, scale, causal=False, q_pos=0, k_pos=0, out=None, ls
 
 def merge(o, lse, o_part, lse_part):
     """Merges (o_part, lse_part) into (o, lse) in place and returns them."""
-    import torch
     _check_qkv(o, o_part)
     B, H, N, D = o.shape
-    for t in (lse, lse_part):
-        if (not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != (B, H, N)
-                or t.dtype != torch.float32):
-            raise ValueError("LSE tensors must be contiguous float32 (B, H, N) device tensors")
+    _check_lse(lse, B, H, N, o)
+    _check_lse(lse_part, B, H, N, o, "lse_part")
     rc = fa_merge(_dtype_code(o), B, H, N, D, o.data_ptr(), lse.data_ptr(), o_part.data_ptr(),
                   lse_part.data_ptr(), _stream())
     if rc != FA_OK:
@@ -204,16 +225,22 @@ def backward(q, k, v, o, do, lse, scale, causal=False, dq=None, dk=None, dv=None
     """(dQ, dK, dV) of sum(O * dO), recomputing P from LSE."""
     import torch
     B, H, N, D = _check_qkv(q, k, v, o, do)
+    _check_lse(lse, B, H, N, q)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check_out(t, q, name)
     need = workspace_bytes(q, causal)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if (not workspace.is_cuda or not workspace.is_contiguous()
+            or workspace.device != q.device):
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
     rc = fa_bwd(_dtype_code(q), B, H, N, D, float(scale), causal, q.data_ptr(), k.data_ptr(),
                 v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
-                dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
-                _stream())
+                dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                workspace.numel() * workspace.element_size(), _stream())
     if rc != FA_OK:
         raise FAError(rc, "fa_bwd")
     return dq, dk, dv

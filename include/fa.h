@@ -17,10 +17,16 @@
  *     keys share N (fa_fwd_partial alone takes separate query and key
  *     lengths).  B * H * N <= 2^30 rows per tensor.
  *   - All tensor pointers are DEVICE pointers owned by the caller and must be
- *     16-byte aligned.  The library never allocates, frees or synchronises;
- *     it only enqueues kernels on `stream` (a hipStream_t; NULL = the null
- *     stream) and returns.  Device faults surface at the caller's next
- *     synchronisation.
+ *     16-byte aligned.  The compute entry points never allocate, free or
+ *     synchronise; they only enqueue kernels on `stream` (a hipStream_t;
+ *     NULL = the null stream) and return.  Device faults surface at the
+ *     caller's next synchronisation.  The exception is the optional timing
+ *     support at the end of this header: fa_timing_enable creates its event
+ *     pool (2 x 8192 hipEvents, once per process) and, while timing is on,
+ *     every launch records two events on its stream; fa_timing_read and
+ *     fa_timing_enable synchronise on recorded events.
+ *   - Grid limit: B * H * ceil(N / 64) < 2^23 (every launch stays below 2^32
+ *     work-items), besides B * H * N <= 2^30.
  *   - Arguments are validated before any HIP call; on an error nothing is
  *     launched and no output is touched.
  *   - causal != 0 keeps key j for query i iff j <= i (diagonal included).
@@ -51,7 +57,7 @@ typedef enum {
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, B/H/N <= 0, N > 2^23, B*H*N > 2^30,
-                               bad scale, negative position                                    */
+                               B*H*ceil(N/64) >= 2^23, bad scale, negative position            */
   FA_ERR_UNSUPPORTED = -2,  /* D not in {64, 128} or unknown dtype                         */
   FA_ERR_WORKSPACE = -3,    /* backward workspace missing or smaller than required          */
   FA_ERR_HIP = -4           /* a kernel launch failed (hipGetLastError after the launch)    */
@@ -165,9 +171,11 @@ int fa_version(void);
  * stream; fa_timing_read synchronises those events and returns, for one
  * kernel id, the number of timed launches and their summed duration in
  * milliseconds.  fa_timing_enable(1) also clears previous totals.  Events
- * come from a fixed pool of 8192 pairs created at enable time (fa_fwd and
- * fa_fwd_partial both count as FA_KERNEL_FWD); launches
- * beyond it are not timed (counted in *dropped).
+ * come from a fixed pool of 8192 pairs created at the first enable (fa_fwd
+ * and fa_fwd_partial both count as FA_KERNEL_FWD); launches beyond it are not
+ * timed (counted in *dropped).  Reading drains the recorded pairs and frees
+ * their slots once no launch holds one.  The records add a little host work
+ * to each launch: time whole steps with timing off.
  */
 enum {
   FA_KERNEL_FWD = 0,          /* forward kernel                          */

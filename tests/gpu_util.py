@@ -8,11 +8,14 @@ from exact_io_aware_58_amd import inputs
 
 # Tolerances.  fp32: max abs 1e-5 on O and LSE.  16-bit storage: max abs
 # 2e-2 on O; dQ, dK, dV max|err| / max|ref| <= 5e-2 per tensor; LSE (fp32
-# output computed from fp32 scores) max abs 1e-3.
+# output computed from fp32 scores) max abs 1e-3.  O is also held to
+# max|err| / max|ref| <= 2e-2 per tensor: with N(0, 1) inputs |O| shrinks
+# like 1/sqrt(N), and at N = 16384 the largest |O| is below 2e-2, where the
+# absolute bound alone would accept O = 0.
 TOL = {
-    "f32": dict(o=1e-5, lse=1e-5),
-    "bf16": dict(o=2e-2, lse=1e-3, grad_rel=5e-2),
-    "f16": dict(o=2e-2, lse=1e-3, grad_rel=5e-2),
+    "f32": dict(o=1e-5, lse=1e-5, o_rel=2e-2),
+    "bf16": dict(o=2e-2, lse=1e-3, grad_rel=5e-2, o_rel=2e-2),
+    "f16": dict(o=2e-2, lse=1e-3, grad_rel=5e-2, o_rel=2e-2),
 }
 
 
@@ -51,6 +54,12 @@ def rel_to_max(a, ref):
     ref = np.asarray(ref)
     den = float(np.max(np.abs(ref))) if ref.size else 0.0
     return max_abs(a, ref) / den if den > 0 else max_abs(a, ref)
+
+
+def o_ok(got, ref, dtype):
+    """(max abs error, error relative to max|ref|, both within TOL[dtype])."""
+    ea, er = max_abs(got, ref), rel_to_max(got, ref)
+    return ea, er, (ea <= TOL[dtype]["o"] and er <= TOL[dtype]["o_rel"])
 
 
 def say(msg):

@@ -65,6 +65,9 @@ def test_version_and_status_strings(fa):
     (dict(N=0), -1),
     (dict(N=1 << 25), -1),
     (dict(B=1 << 10, H=1 << 10, N=1 << 11), -1),  # B*H*N > 2^30
+    (dict(B=1, H=1 << 23, N=1), -1),   # B*H*ceil(N/64) = 2^23: a grid of 2^32 work-items
+    (dict(B=1 << 12, H=1 << 11, N=64), -1),
+    (dict(B=1 << 10, H=1 << 10, N=520), -1),  # 2^20 heads x 9 padded 64-row blocks
     (dict(scale=0.0), -1),
     (dict(scale=-0.125), -1),
     (dict(scale=float("inf")), -1),
@@ -171,3 +174,33 @@ def test_merge_validation(fa):
             ptrs = list(ok)
             ptrs[which] = bad
             assert fa.fa_merge(fa.FA_F16, 1, 2, 100, 64, *ptrs, None) == fa.FA_ERR_INVALID_ARG
+
+
+class _FakeTensor:
+    """Stands in for a device tensor in the binding's argument checks (no
+    GPU here): only the attributes the checks read."""
+
+    def __init__(self, shape, dtype, cuda=True, contiguous=True, device="cuda:0"):
+        self.shape, self.dtype, self.is_cuda, self.device = tuple(shape), dtype, cuda, device
+        self._contiguous = contiguous
+
+    def is_contiguous(self):
+        return self._contiguous
+
+
+def test_binding_rejects_bad_caller_outputs(fa):
+    torch = pytest.importorskip("torch")
+    q = _FakeTensor((1, 2, 64, 64), torch.bfloat16)
+    fa._check_out(_FakeTensor(q.shape, q.dtype), q, "out")
+    for bad in (_FakeTensor((1, 2, 32, 64), q.dtype), _FakeTensor(q.shape, torch.float16),
+                _FakeTensor(q.shape, q.dtype, contiguous=False),
+                _FakeTensor(q.shape, q.dtype, cuda=False, device="cpu"),
+                _FakeTensor(q.shape, q.dtype, device="cuda:1")):
+        with pytest.raises(ValueError):
+            fa._check_out(bad, q, "out")
+    fa._check_lse(_FakeTensor((1, 2, 64), torch.float32), 1, 2, 64, q)
+    for bad in (_FakeTensor((1, 2, 64), torch.bfloat16), _FakeTensor((1, 2, 63), torch.float32),
+                _FakeTensor((1, 2, 64), torch.float32, contiguous=False),
+                _FakeTensor((1, 2, 64), torch.float32, device="cuda:1")):
+        with pytest.raises(ValueError):
+            fa._check_lse(bad, 1, 2, 64, q)

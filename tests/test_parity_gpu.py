@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from exact_io_aware_58_amd import inputs
-from tests.gpu_util import TOL, draw_case, max_abs, rel_to_max, say, to_f64
+from tests.gpu_util import TOL, draw_case, max_abs, o_ok, rel_to_max, say, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -258,9 +258,10 @@ def test_workload_c2_bf16_forward():
     vals, devs = _workload_devs(w)
     o, lse = _fwd(devs, w.scale, w.causal)
     ro, rl = oracle.attention_fwd(vals["q"], vals["k"], vals["v"], w.scale, w.causal)
-    eo, el = max_abs(to_f64(o), ro), max_abs(to_f64(lse), rl)
-    say(f"    max abs O={eo:.2e} (rel-to-max {rel_to_max(to_f64(o), ro):.2e}) LSE={el:.2e}")
-    assert eo <= 2e-2 and el <= 1e-3
+    eo, er, ok = o_ok(to_f64(o), ro, "bf16")
+    el = max_abs(to_f64(lse), rl)
+    say(f"    max abs O={eo:.2e} (rel-to-max {er:.2e}) LSE={el:.2e}")
+    assert ok and el <= 1e-3
 
 
 def test_workload_c3_causal_training_step():
@@ -272,10 +273,11 @@ def test_workload_c3_causal_training_step():
     torch.cuda.synchronize()
     ro, rl = oracle.attention_fwd(vals["q"], vals["k"], vals["v"], w.scale, True)
     rq, rk, rv = oracle.attention_bwd(vals["q"], vals["k"], vals["v"], vals["do"], w.scale, True)
-    eo, el = max_abs(to_f64(o), ro), max_abs(to_f64(lse), rl)
+    eo, er, ok = o_ok(to_f64(o), ro, "bf16")
+    el = max_abs(to_f64(lse), rl)
     eq, ek, ev = rel_to_max(to_f64(dq), rq), rel_to_max(to_f64(dk), rk), rel_to_max(to_f64(dv), rv)
-    say(f"    O={eo:.2e} LSE={el:.2e} dQ={eq:.2e} dK={ek:.2e} dV={ev:.2e}")
-    assert eo <= 2e-2 and el <= 1e-3
+    say(f"    O={eo:.2e} (rel-to-max {er:.2e}) LSE={el:.2e} dQ={eq:.2e} dK={ek:.2e} dV={ev:.2e}")
+    assert ok and el <= 1e-3
     assert eq <= 5e-2 and ek <= 5e-2 and ev <= 5e-2
 
 
@@ -296,10 +298,11 @@ def test_workload_c4_long_forward_subset():
     assert peak_extra <= o.numel() * 2 + lse.numel() * 4 + (1 << 21)
     rows = inputs.check_row_subset(w)
     ro, rl = oracle.attention_fwd_rows(vals["q"], vals["k"], vals["v"], w.scale, w.causal, rows)
-    eo = max_abs(_sampled(o, rows), ro)
+    eo, er, ok = o_ok(_sampled(o, rows), ro, "bf16")
     el = max_abs(to_f64(lse)[tuple(rows.T)], rl)
-    say(f"    {len(rows)} rows: max abs O={eo:.2e} LSE={el:.2e}")
-    assert eo <= 2e-2 and el <= 1e-3
+    say(f"    {len(rows)} rows: max abs O={eo:.2e} (rel-to-max {er:.2e}, max |O_ref| "
+        f"{np.max(np.abs(ro)):.3e}) LSE={el:.2e}")
+    assert ok and el <= 1e-3
 
 
 def _key_rows_two_heads(w, count=128):
@@ -330,10 +333,10 @@ def test_workload_c5_long_causal_training_subset():
     ro, rl = oracle.attention_fwd_rows(vals["q"], vals["k"], vals["v"], w.scale, True, qrows)
     rq = oracle.attention_bwd_query_rows(vals["q"], vals["k"], vals["v"], vals["do"], w.scale,
                                          True, qrows)
-    eo = max_abs(_sampled(o, qrows), ro)
+    eo, er, ok = o_ok(_sampled(o, qrows), ro, "bf16")
     el = max_abs(to_f64(lse)[tuple(qrows.T)], rl)
     eq = rel_to_max(_sampled(dq, qrows), rq)
-    say(f"    {len(qrows)} query rows: O={eo:.2e} LSE={el:.2e} dQ={eq:.2e}")
+    say(f"    {len(qrows)} query rows: O={eo:.2e} (rel-to-max {er:.2e}) LSE={el:.2e} dQ={eq:.2e}")
     krows = _key_rows_two_heads(w)
     stats = {}
     for h in sorted({int(r[1]) for r in krows}):
@@ -344,7 +347,7 @@ def test_workload_c5_long_causal_training_subset():
                                            True, krows, stats=stats)
     ek, ev = rel_to_max(_sampled(dk, krows), rk), rel_to_max(_sampled(dv, krows), rv)
     say(f"    {len(krows)} key rows: dK={ek:.2e} dV={ev:.2e}")
-    assert eo <= 2e-2 and el <= 1e-3 and eq <= 5e-2
+    assert ok and el <= 1e-3 and eq <= 5e-2
     assert ek <= 5e-2 and ev <= 5e-2
 
 
@@ -361,19 +364,19 @@ def test_workload_n128k_causal_training_subset():
     dq, dk, dv = fa.backward(devs["q"], devs["k"], devs["v"], o, devs["do"], lse, w.scale, True)
     torch.cuda.synchronize()
     peak_extra = torch.cuda.max_memory_allocated() - before
-    # outputs (O, dQ, dK, dV, LSE) and the workspace (row statistics and, at
-    # D = 64, transposed copies of Q, dO, K: all linear in N); nothing N x N
+    # outputs (O, dQ, dK, dV, LSE) and the workspace (two float32 row
+    # statistics per query row, -Delta and -LSE/scale); nothing N x N
     ws = fa.workspace_bytes(devs["q"], True)
-    assert ws <= 3 * o.numel() * 2 + 2 * lse.numel() * 4 + (1 << 20)
+    assert ws <= 2 * lse.numel() * 4 + 512
     assert peak_extra <= 4 * o.numel() * 2 + lse.numel() * 4 + ws + (1 << 22)
     qrows = inputs.check_row_subset(w)
     ro, rl = oracle.attention_fwd_rows(vals["q"], vals["k"], vals["v"], w.scale, True, qrows)
     rq = oracle.attention_bwd_query_rows(vals["q"], vals["k"], vals["v"], vals["do"], w.scale,
                                          True, qrows)
-    eo = max_abs(_sampled(o, qrows), ro)
+    eo, er, ok = o_ok(_sampled(o, qrows), ro, "bf16")
     el = max_abs(to_f64(lse)[tuple(qrows.T)], rl)
     eq = rel_to_max(_sampled(dq, qrows), rq)
-    say(f"    {len(qrows)} query rows: O={eo:.2e} LSE={el:.2e} dQ={eq:.2e}")
+    say(f"    {len(qrows)} query rows: O={eo:.2e} (rel-to-max {er:.2e}) LSE={el:.2e} dQ={eq:.2e}")
     krows = np.array([r for r in _key_rows_two_heads(w, count=48) if r[1] == 0][:32], dtype=np.int64)
     say("    oracle row statistics of head 0 ...")
     stats = {(0, 0): oracle.row_stats(vals["q"], vals["k"], vals["v"], vals["do"], w.scale, True,
@@ -382,5 +385,5 @@ def test_workload_n128k_causal_training_subset():
                                            True, krows, stats=stats)
     ek, ev = rel_to_max(_sampled(dk, krows), rk), rel_to_max(_sampled(dv, krows), rv)
     say(f"    {len(krows)} key rows: dK={ek:.2e} dV={ev:.2e}")
-    assert eo <= 2e-2 and el <= 1e-3 and eq <= 5e-2
+    assert ok and el <= 1e-3 and eq <= 5e-2
     assert ek <= 5e-2 and ev <= 5e-2

@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 from exact_io_aware_58_amd import inputs
-from tests.gpu_util import TOL, max_abs, say, to_device, to_f64
+from tests.gpu_util import TOL, max_abs, o_ok, say, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -206,7 +206,7 @@ def test_long_sequence_split_four_ways_subset():
     ro, rl = oracle.attention_fwd_rows(vals["q"], vals["k"], vals["v"], w.scale, True, rows)
     idx = torch.from_numpy(rows).to(o.device)
     got_o = to_f64(o[idx[:, 0], idx[:, 1], idx[:, 2]])
-    eo = max_abs(got_o, ro)
+    eo, er, ok = o_ok(got_o, ro, "bf16")
     el = max_abs(to_f64(lse)[tuple(rows.T)], rl)
-    say(f"    {len(rows)} rows: max abs O={eo:.2e} LSE={el:.2e}")
-    assert eo <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"]
+    say(f"    {len(rows)} rows: max abs O={eo:.2e} (rel-to-max {er:.2e}) LSE={el:.2e}")
+    assert ok and el <= TOL["bf16"]["lse"]
