@@ -5,8 +5,20 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fa.h"
 #include "fa_launch.h"
+
+// ---- fixed device scratch for fa_bwd_noalloc ----
+// Holds the two float32 row arrays fa_bwd keeps in the caller's workspace.
+// A file-scope device array: every GPU the library runs on holds one copy,
+// allocated when the code object is loaded, until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device copy: its
+// device address is looked up once per device with hipGetSymbolAddress and
+// only that address is handed to kernels.
+constexpr size_t kScratchBytes = size_t(32) << 20;  // 32 MiB: B*H*N up to 2^22 rows
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -41,9 +53,29 @@ size_t delta_bytes(int B, int H, int N) {
   return (n + 255) & ~(size_t)255;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch (the current device, which must be
+// the one the caller's stream belongs to); looked up on the first call on a
+// device.
+int device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
 }  // namespace
 
-extern "C" int fa_version(void) { return 2; }
+extern "C" int fa_version(void) { return 3; }
 
 extern "C" const char* fa_status_string(int status) {
   switch (status) {
@@ -123,23 +155,23 @@ extern "C" size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int D, 
   return 2 * delta_bytes(B, H, N);
 }
 
-extern "C" int fa_bwd(int dtype, int B, int H, int N, int D, float scale, int causal,
-                      const void* Q, const void* K, const void* V, const void* O,
-                      const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Validation shared by fa_bwd and fa_bwd_noalloc.
+int check_bwd(int dtype, int B, int H, int N, int D, float scale, const void* Q, const void* K,
+              const void* V, const void* O, const void* dO, const float* LSE, const void* dQ,
+              const void* dK, const void* dV) {
   int rc = check_problem(dtype, B, H, N, D, scale);
   if (rc != FA_OK) return rc;
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;  // backward kernels are 16-bit only
   const void* ptrs[] = {Q, K, V, O, dO, LSE, dQ, dK, dV};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_INVALID_ARG;
-  const size_t rows_bytes = delta_bytes(B, H, N);
-  if (!workspace || workspace_bytes < 2 * rows_bytes) return FA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
-  float* ndelta = (float*)workspace;
-  float* nlse = (float*)((char*)workspace + rows_bytes);
-  fa::BwdArgs a{dtype, B, H, N, D, scale, causal ? 1 : 0, Q, K, V, O, dO, LSE,
-                dQ, dK, dV, ndelta, nlse, (hipStream_t)stream};
+  return FA_OK;
+}
+
+// The three backward kernels on `a.stream`.
+int launch_bwd(const fa::BwdArgs& a) {
   hipError_t e;
   {
     fa::TimedLaunch t(FA_KERNEL_BWD_DELTA, a.stream);
@@ -156,4 +188,44 @@ extern "C" int fa_bwd(int dtype, int B, int H, int N, int D, float scale, int ca
     e = fa::launch_bwd_dq(a);
   }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int fa_bwd(int dtype, int B, int H, int N, int D, float scale, int causal,
+                      const void* Q, const void* K, const void* V, const void* O,
+                      const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_bwd(dtype, B, H, N, D, scale, Q, K, V, O, dO, LSE, dQ, dK, dV);
+  if (rc != FA_OK) return rc;
+  const size_t rows_bytes = delta_bytes(B, H, N);
+  if (!workspace || workspace_bytes < 2 * rows_bytes) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
+  float* ndelta = (float*)workspace;
+  float* nlse = (float*)((char*)workspace + rows_bytes);
+  fa::BwdArgs a{dtype, B, H, N, D, scale, causal ? 1 : 0, Q, K, V, O, dO, LSE,
+                dQ, dK, dV, ndelta, nlse, (hipStream_t)stream};
+  return launch_bwd(a);
+}
+
+extern "C" size_t fa_bwd_noalloc_max_bytes(void) { return kScratchBytes; }
+
+extern "C" int fa_bwd_noalloc(int dtype, int B, int H, int N, int D, float scale, int causal,
+                              const void* Q, const void* K, const void* V, const void* O,
+                              const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                              void* stream) {
+  int rc = check_bwd(dtype, B, H, N, D, scale, Q, K, V, O, dO, LSE, dQ, dK, dV);
+  if (rc != FA_OK) return rc;
+  const size_t rows_bytes = delta_bytes(B, H, N);
+  if (2 * rows_bytes > kScratchBytes) return FA_ERR_WORKSPACE;
+  void* base = nullptr;
+  rc = device_scratch(&base);
+  if (rc != FA_OK) return rc;
+  // Every element the kernels read from the scratch is written first by the
+  // Delta kernel of this same call, so nothing needs clearing.
+  float* ndelta = (float*)base;
+  float* nlse = (float*)((char*)base + rows_bytes);
+  fa::BwdArgs a{dtype, B, H, N, D, scale, causal ? 1 : 0, Q, K, V, O, dO, LSE,
+                dQ, dK, dV, ndelta, nlse, (hipStream_t)stream};
+  return launch_bwd(a);
 }

@@ -30,6 +30,8 @@ SIGNATURES = {
     "fa_merge": (_c_int, [_c_int] * 5 + [_vp] * 5),
     "fa_bwd_workspace_bytes": (_c_size, [_c_int] * 6),
     "fa_bwd": (_c_int, [_c_int] * 5 + [_f, _c_int] + [_vp] * 10 + [_c_size, _vp]),
+    "fa_bwd_noalloc": (_c_int, [_c_int] * 5 + [_f, _c_int] + [_vp] * 10),
+    "fa_bwd_noalloc_max_bytes": (_c_size, []),
     "fa_status_string": (ctypes.c_char_p, [_c_int]),
     "fa_version": (_c_int, []),
     "fa_timing_enable": (_c_int, [_c_int]),
@@ -85,6 +87,16 @@ def fa_bwd(dtype, B, H, N, D, scale, causal, Q, K, V, O, dO, LSE, dQ, dK, dV,
            workspace, workspace_bytes, stream) -> int:
     return _lib.fa_bwd(dtype, B, H, N, D, scale, int(causal), Q, K, V, O, dO, LSE,
                        dQ, dK, dV, workspace, workspace_bytes, stream)
+
+
+def fa_bwd_noalloc(dtype, B, H, N, D, scale, causal, Q, K, V, O, dO, LSE, dQ, dK, dV,
+                   stream) -> int:
+    return _lib.fa_bwd_noalloc(dtype, B, H, N, D, scale, int(causal), Q, K, V, O, dO, LSE,
+                               dQ, dK, dV, stream)
+
+
+def fa_bwd_noalloc_max_bytes() -> int:
+    return _lib.fa_bwd_noalloc_max_bytes()
 
 
 def fa_status_string(status: int) -> str:

@@ -159,6 +159,33 @@ int fa_bwd(int dtype, int B, int H, int N, int D, float scale, int causal,
            const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory
+ * (code recorded into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results as fa_bwd, bit for bit, with the
+ * workspace taken from a fixed scratch buffer the library holds on each GPU
+ * (a device array of fa_bwd_noalloc_max_bytes() bytes, allocated when the
+ * library's code is loaded on that GPU and kept until the process ends).
+ * Allocates, frees and synchronises nothing.
+ *
+ *   Arguments as fa_bwd, without workspace and workspace_bytes.  The stream
+ *   must belong to the current device (the one whose scratch is used).
+ *   Returns FA_ERR_WORKSPACE if fa_bwd_workspace_bytes(...) for the problem
+ *   exceeds fa_bwd_noalloc_max_bytes() (B * H * N above 2^22 rows), and
+ *   FA_ERR_HIP if the scratch's device address cannot be looked up.
+ *   All calls on one GPU share its scratch: calls that overlap in time on
+ *   one GPU (several streams or threads) race and must be serialised by the
+ *   caller.  The scratch keeps the last call's row statistics; every value a
+ *   call reads is written earlier in the same call.
+ */
+int fa_bwd_noalloc(int dtype, int B, int H, int N, int D, float scale, int causal,
+                   const void* Q, const void* K, const void* V, const void* O,
+                   const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                   void* stream);
+
+/* Size in bytes of the fixed scratch fa_bwd_noalloc uses on each GPU. */
+size_t fa_bwd_noalloc_max_bytes(void);
+
 /* Static English text for a status code. */
 const char* fa_status_string(int status);
 

@@ -204,3 +204,26 @@ def test_binding_rejects_bad_caller_outputs(fa):
                 _FakeTensor((1, 2, 64), torch.float32, device="cuda:1")):
         with pytest.raises(ValueError):
             fa._check_lse(bad, 1, 2, 64, q)
+
+
+def test_noalloc_backward_validation(fa):
+    """Argument checks of fa_bwd_noalloc happen before any HIP call."""
+    cap = fa.fa_bwd_noalloc_max_bytes()
+    assert cap == 32 << 20
+    # the scratch holds the workspace of 2^22 rows and no more
+    assert fa.fa_bwd_workspace_bytes(fa.FA_BF16, 1, 64, 65536, 64, 1) == cap
+    assert fa.fa_bwd_workspace_bytes(fa.FA_BF16, 1, 65, 65536, 64, 1) > cap
+
+    def call(dtype=fa.FA_BF16, H=2, N=128, D=64, scale=0.125, ptr_over=None):
+        ptrs = P[:9]
+        if ptr_over:
+            ptrs[ptr_over[0]] = ptr_over[1]
+        return fa.fa_bwd_noalloc(dtype, 1, H, N, D, scale, 0, *ptrs, None)
+
+    assert call(H=65, N=65536) == fa.FA_ERR_WORKSPACE
+    assert call(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert call(D=80) == fa.FA_ERR_UNSUPPORTED
+    assert call(scale=0.0) == fa.FA_ERR_INVALID_ARG
+    for i in range(9):
+        assert call(ptr_over=(i, 0)) == fa.FA_ERR_INVALID_ARG
+        assert call(ptr_over=(i, A + 2)) == fa.FA_ERR_INVALID_ARG
