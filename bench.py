@@ -9,12 +9,19 @@ D=64, bf16, seeded i.i.d. N(0, 1) inputs already resident in HBM.
 
 Prints ONE JSON line.  ``value`` is algorithmic TFLOP/s of the step:
 forward 4*B*H*N^2*D and backward 10*B*H*N^2*D, both halved under the causal
-mask, divided by the step time measured with HIP events on the launch stream.
-The ``roofline`` object covers the kernel that takes the most time; its
-duration comes from per-launch HIP events recorded by the library on the
-same stream during the timed steps.  ``cpu_baseline`` times the float64
-oracle on a bounded sample (the leading R x R causal block of head 0) on
-the host cores.
+mask, divided by the mean step time measured with HIP events on the launch
+stream (``step_ms`` adds the median and minimum of the per-step times).  The
+``roofline`` object covers the kernel that takes the most time; its average
+duration comes from per-launch HIP events that the library records on the
+same stream during a second run of as many steps (kept out of the headline
+steps).  ``sclk`` is the shader clock the driver reports while further steps
+run back to back after both timed regions (the chip holds a clock below its
+2.4 GHz peak at its power limit), and the ``*_at_measured_clock`` fields
+scale the peak to it.  ``secondary`` times other workloads launch by launch (c2, c3, the
+D = 128 forwards at N = 4096, 8192 and 16384, a D = 128 training step).
+``cpu_baseline`` times the float64 oracle on a bounded sample (the leading
+R x R causal block of head 0) on the host cores, with an extrapolation of
+the whole workload's oracle time.
 """
 from __future__ import annotations
 
@@ -65,7 +72,7 @@ def kernel_algorithmic(w):
 KERNEL_SOURCES = {
     "fwd": ["fa_fwd.hip", "fa_device.h"],
     "bwd_delta": ["fa_bwd.hip", "fa_device.h"],
-    "bwd_dkdv": ["fa_bwd.hip", "fa_device.h"],
+    "bwd_dkdv": ["fa_bwd.hip", "fa_bwd_dkdv.h", "fa_bwd_d128.hip", "fa_device.h"],
     "bwd_dq": ["fa_bwd.hip", "fa_device.h"],
     "merge": ["fa_merge.hip", "fa_device.h"],
 }
@@ -104,7 +111,15 @@ def upload(raw, dtype):
     return torch.from_numpy(np.ascontiguousarray(raw)).cuda()
 
 
-def run_gpu(w, steps, warmup):
+def run_gpu(w, steps, warmup, clock=None, clock_window_s=3.5):
+    """Headline: `warmup` untimed steps, then `steps` steps between a
+    synchronisation and an event on each side, one event between consecutive
+    steps (per-step durations for the median and minimum); per-kernel event
+    timing is off here.  Then the same number of steps again with the
+    library's per-kernel events on, for the per-kernel averages.  Then, with
+    a ClockSampler, steps back to back for `clock_window_s` seconds while it
+    reads the shader clock.  Returns (ms per step, per-step times, per-kernel
+    dict, ms per step of the second pass, clock summary or None)."""
     import torch
     from exact_io_aware_58_amd import fa, inputs
 
@@ -141,58 +156,137 @@ def run_gpu(w, steps, warmup):
         step()
     torch.cuda.synchronize()
     log(f"[bench] warmup {warmup} done; timing {steps} steps")
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    fa.fa_timing_enable(True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(steps):
+    ev[0].record(stream)
+    for i in range(steps):
         step()
-    end.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
+    total_ms = ev[0].elapsed_time(ev[-1])
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    log(f"[bench] {steps} steps in {total_ms:.3f} ms")
+
+    kreps = max(steps, 3)
+    fa.fa_timing_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(kreps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    timed_ms = e0.elapsed_time(e1) / kreps
+    clk = None
+    if clock is not None and clock_window_s > 0:
+        # the clock the chip holds under this load: more steps back to back
+        # (outside both timed regions) while the sampler reads the driver
+        clock.start()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < clock_window_s:
+            for _ in range(4):
+                step()
+            torch.cuda.synchronize()
+        clock.stop()
+        clk = clock.summary(time.perf_counter() - t0)
     kernels = {}
     for kid in range(fa.FA_KERNEL_COUNT):
         n, ms, dropped = fa.fa_timing_read(kid)
         if n:
             kernels[fa.fa_kernel_name(kid)] = {"launches": n, "avg_ms": ms / n}
     fa.fa_timing_enable(False)
-    log(f"[bench] {steps} steps in {total_ms:.3f} ms")
-    return total_ms / steps, kernels
+    log(f"[bench] per-kernel pass: {kreps} steps, {timed_ms:.3f} ms per step")
+    return total_ms / steps, per_step, kernels, timed_ms, clk
 
 
-def run_fwd_launches(w, reps, warmup):
-    """Forward-only workload `w`: `warmup` untimed launches, then `reps`
-    launches each bracketed by its own pair of events on the launch stream.
-    Returns the per-launch times in ms."""
+def run_secondary(w, reps=20, warmup=5):
+    """One workload timed launch by launch: `warmup` untimed passes, then
+    `reps` launches of fa_fwd (and, with a backward, `reps` of fa_bwd after
+    them), each between the events recorded before and after it on the
+    launch stream (mean, median, minimum), then `reps` more between two
+    events only (``batch_ms``: short kernels lose a few microseconds to the
+    events between launches).
+    Returns a dict with mean, median and minimum per pass and the rates."""
+    import statistics
+
     import torch
     from exact_io_aware_58_amd import fa, inputs
 
-    devs = {n: upload(raw, w.dtype) for n, (_, raw) in inputs.make_inputs(w).items()
-            if n in ("q", "k", "v")}
+    devs = {n: upload(raw, w.dtype) for n, (_, raw) in inputs.make_inputs(w).items()}
+    q, k, v = devs["q"], devs["k"], devs["v"]
     code = {"f32": fa.FA_F32, "bf16": fa.FA_BF16, "f16": fa.FA_F16}[w.dtype]
-    o = torch.empty_like(devs["q"])
+    o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    args_f = (code, w.B, w.H, w.N, w.D, w.scale, w.causal, devs["q"].data_ptr(),
-              devs["k"].data_ptr(), devs["v"].data_ptr(), o.data_ptr(), lse.data_ptr(),
-              stream.cuda_stream)
+    sh = stream.cuda_stream
+    args_f = (code, w.B, w.H, w.N, w.D, w.scale, w.causal, q.data_ptr(), k.data_ptr(),
+              v.data_ptr(), o.data_ptr(), lse.data_ptr(), sh)
 
-    def launch():
+    def fwd():
         rc = fa.fa_fwd(*args_f)
         if rc != fa.FA_OK:
             raise fa.FAError(rc, "fa_fwd")
 
-    for _ in range(warmup):
-        launch()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    torch.cuda.synchronize()
-    for e0, e1 in ev:
+    def timed(fn):
+        # launches enqueued back to back with one event between consecutive
+        # launches, so the GPU's queue never waits for the host; then the
+        # same number of launches between just two events (no event work
+        # between kernels: the rate the kernels sustain when queued)
+        for _ in range(warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(reps):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        launch()
+        for _ in range(reps):
+            fn()
         e1.record(stream)
-    torch.cuda.synchronize()
-    return [e0.elapsed_time(e1) for e0, e1 in ev]
+        torch.cuda.synchronize()
+        return per, e0.elapsed_time(e1) / reps
+
+    f, b = flops(w)
+    out = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "dtype": w.dtype,
+           "causal": w.causal, "input_mult": w.input_mult, "launches": reps, "warmup": warmup}
+
+    def summary(res, work):
+        t, batch = res
+        mean, med, mn = statistics.mean(t), statistics.median(t), min(t)
+        return {"ms": mean, "median_ms": med, "min_ms": mn,
+                "tflops": work / mean / 1e9, "tflops_median": work / med / 1e9,
+                "pct_of_bf16_peak": 100.0 * work / mean / 1e9 / PEAK_BF16_TFLOPS,
+                "pct_of_bf16_peak_median": 100.0 * work / med / 1e9 / PEAK_BF16_TFLOPS,
+                "batch_ms": batch, "tflops_batch": work / batch / 1e9,
+                "pct_of_bf16_peak_batch": 100.0 * work / batch / 1e9 / PEAK_BF16_TFLOPS}
+
+    out["fwd"] = summary(timed(fwd), f)
+    if w.backward:
+        do = devs["do"]
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        wsb = fa.fa_bwd_workspace_bytes(code, w.B, w.H, w.N, w.D, w.causal)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+        fwd()
+        args_b = (code, w.B, w.H, w.N, w.D, w.scale, w.causal, q.data_ptr(), k.data_ptr(),
+                  v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                  dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), wsb, sh)
+
+        def bwd():
+            rc = fa.fa_bwd(*args_b)
+            if rc != fa.FA_OK:
+                raise fa.FAError(rc, "fa_bwd")
+
+        out["bwd"] = summary(timed(bwd), b)
+        del dq, dk, dv, ws
+    log(f"[bench] {w.name}: fwd median {out['fwd']['median_ms']:.4f} ms"
+        + (f", bwd median {out['bwd']['median_ms']:.4f} ms" if w.backward else ""))
+    del devs, q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_split(w, parts, reps=3):
@@ -262,40 +356,66 @@ def run_split(w, parts, reps=3):
     }
 
 
+def blas_info():
+    """(vendor and version of the BLAS numpy calls, threads it uses)."""
+    try:
+        from threadpoolctl import threadpool_info
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    except Exception:  # pragma: no cover
+        pools = []
+    if not pools:
+        return "unknown", 1
+    p = pools[0]
+    return f"{p.get('internal_api', '?')} {p.get('version', '')}".strip(), int(p.get("num_threads", 1))
+
+
 def cpu_baseline(w, rows):
     """The float64 oracle on the leading rows x rows block of head 0 (causal:
     those queries see only those keys, so the block is a self-contained slice
-    of the workload), forward + backward."""
+    of the workload), forward + backward, with the BLAS thread pool set to
+    the CPUs this process may run on.  Also reports the whole workload's
+    oracle time extrapolated by flops from the sample (labelled as such)."""
     import numpy as np
     import oracle
     from exact_io_aware_58_amd import inputs
+    affinity = len(os.sched_getaffinity(0))
+    limiter = None
     try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=affinity, user_api="blas")
     except Exception:  # pragma: no cover
-        cores = 1
+        pass
+    vendor, threads = blas_info()
     rows = min(rows, w.N)
     t = {}
     for name in ("q", "k", "v", "do"):
         x, _ = inputs.draw(w.seed, name, w.shape, w.dtype, w.input_mult if name != "do" else 1.0)
         t[name] = x[:1, :1, :rows].astype(np.float64)
-    log(f"[bench] cpu baseline: oracle on head 0, rows [0, {rows}) ...")
+    log(f"[bench] cpu baseline: oracle on head 0, rows [0, {rows}), {threads} BLAS threads "
+        f"({vendor}) ...")
     t0 = time.perf_counter()
     oracle.attention_fwd(t["q"], t["k"], t["v"], w.scale, w.causal)
     if w.backward:
         oracle.attention_bwd(t["q"], t["k"], t["v"], t["do"], w.scale, w.causal)
     sec = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.restore_original_limits()
     sub = type(w)(w.name, w.seed, 1, 1, rows, w.D, w.dtype, w.causal, w.backward)
     f, b = flops(sub)
+    fw, bw = flops(w)
     return {
         "value": (f + b) / sec / 1e12,
         "unit": "TFLOP/s",
-        "cores": cores,
+        "cores": threads,
         "kind": "oracle",
         "sample": f"head 0 of batch 0, leading {rows}x{rows} "
                   f"{'causal ' if w.causal else ''}block, "
                   f"{'fwd+bwd' if w.backward else 'fwd'} in float64 ({sec:.1f} s)",
         "seconds": sec,
+        "affinity_cpus": affinity,
+        "blas": vendor,
+        "extrapolated_full_workload_s": sec * (fw + bw) / (f + b),
+        "extrapolation": "sample seconds x (workload flops / sample flops); not measured",
     }
 
 
@@ -367,17 +487,101 @@ def run_sweep(ns, heads=16, D=64, reps=5):
         torch.cuda.empty_cache()
 
 
+class ClockSampler:
+    """Shader clock while the GPU runs the workload, from the AMD SMI
+    library's copy of the driver's metrics table (current clock of each XCD,
+    averaged over the XCDs).  The table refreshes about once a second, so a
+    thread polls it every 10 ms between start() and stop() and keeps one
+    sample per refresh, dropping the table current at start() and the first
+    refresh after it (which may still cover time before the window).  It
+    makes no HIP call.  summary() is None without the library or samples."""
+
+    def __init__(self, period=0.01):
+        import threading
+        self.period = period
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if handles:
+                self._smi, self._handle = amdsmi, handles[0]
+        except Exception as e:  # pragma: no cover - depends on the box
+            log(f"[bench] no shader-clock samples: {e}")
+
+    def read(self):
+        """(refresh counter, mean current clock over the XCDs in MHz) or None."""
+        try:
+            m = self._smi.amdsmi_get_gpu_metrics_info(self._handle)
+        except Exception:  # pragma: no cover
+            return None
+        vals = [v for v in (m.get("current_gfxclks") or []) if isinstance(v, (int, float)) and v > 0]
+        if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
+            vals = [m["current_gfxclk"]]
+        stamp = m.get("system_clock_counter")
+        return (stamp, sum(vals) / len(vals)) if vals and stamp is not None else None
+
+    def _run(self, first):
+        seen = {first}
+        fresh = 0
+        while not self._stop.is_set():
+            r = self.read()
+            if r is not None and r[0] not in seen:
+                seen.add(r[0])
+                fresh += 1
+                if fresh > 1:
+                    self.samples.append(r[1])
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+        if self._handle is None:
+            return
+        r = self.read()
+        self._stop.clear()
+        self._thread = threading.Thread(target=self._run, args=(r[0] if r else None,),
+                                        daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+            self._thread = None
+
+    def summary(self, window_s):
+        if not self.samples:
+            return None
+        import statistics
+        return {"source": "AMD SMI metrics table (current clock per XCD, averaged), one sample "
+                          "per table refresh while the workload's steps ran back to back",
+                "window_s": window_s, "samples": len(self.samples),
+                "mean_mhz": statistics.mean(self.samples),
+                "min_mhz": min(self.samples), "max_mhz": max(self.samples)}
+
+
+NOMINAL_SCLK_MHZ = 2400.0
+
+SECONDARY = ("c2", "c3", "n4k_d128", "n8k_d128", "c4", "train_d128")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c5", help="c1..c5 (default c5)")
     ap.add_argument("--cpu-rows", type=int, default=32768,
                     help="rows of the oracle sample timed for cpu_baseline (0: skip)")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the N=16384 D=128 forward-only figure and the block-split "
-                         "forward")
+                    help="skip the secondary workloads (c2, c3, D=128 forwards at N=4096, "
+                         "8192, 16384, the D=128 training step) and the block-split forward")
+    ap.add_argument("--clock-window", type=float, default=3.5,
+                    help="seconds of extra steps (outside the timed regions) during which the "
+                         "shader clock is sampled (0: skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size kernel for scaling HBM byte counters)")
@@ -395,11 +599,16 @@ def main():
               "(the attention path is built and timed on a single MI355X)", file=sys.stderr)
         sys.exit(2)
 
+    import statistics
+
     from exact_io_aware_58_amd import inputs
     w = inputs.WORKLOADS[args.workload]
-    ms, kernels = run_gpu(w, args.steps, args.warmup)
+    clock = ClockSampler()
+    ms, per_step, kernels, kernel_pass_ms, clk = run_gpu(w, args.steps, args.warmup, clock,
+                                                         args.clock_window)
     f, b = flops(w)
     value = (f + b) / (ms / 1e3) / 1e12
+    med, mn = statistics.median(per_step), min(per_step)
 
     alg = kernel_algorithmic(w)
     dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
@@ -424,24 +633,22 @@ def main():
     for p in passes.values():
         p["pct_of_bf16_peak"] = 100.0 * p["tflops"] / PEAK_BF16_TFLOPS
 
-    secondary = None
-    if not args.no_secondary and args.workload != "c4":
-        import statistics
-        w4 = inputs.WORKLOADS["c4"]
-        t4 = run_fwd_launches(w4, reps=max(20, args.steps), warmup=max(5, args.warmup))
-        f4, _ = flops(w4)
-        ms4, med4, min4 = statistics.mean(t4), statistics.median(t4), min(t4)
+    roofline = {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak,
+                "unit": unit, "frac": achieved / peak,
+                "traffic": profiled_traffic(w.name, dom)}
+    if clk and bound == "mfma":
+        # the same peak scaled to the shader clock sampled while the steps ran
+        roofline["peak_at_measured_clock"] = peak * clk["mean_mhz"] / NOMINAL_SCLK_MHZ
+        roofline["frac_at_measured_clock"] = achieved / roofline["peak_at_measured_clock"]
 
-        def rate(t):
-            return f4 / (t / 1e3) / 1e12
-
-        secondary = {"workload": w4.name, "pass": "fwd", "launches": len(t4),
-                     "warmup": max(5, args.warmup), "ms": ms4, "median_ms": med4,
-                     "min_ms": min4, "tflops": rate(ms4), "tflops_median": rate(med4),
-                     "pct_of_bf16_peak": 100.0 * rate(ms4) / PEAK_BF16_TFLOPS,
-                     "pct_of_bf16_peak_median": 100.0 * rate(med4) / PEAK_BF16_TFLOPS}
-        log(f"[bench] {w4.name}: mean {ms4:.3f} ms, median {med4:.3f} ms, min {min4:.3f} ms "
-            f"over {len(t4)} launches")
+    secondary = {}
+    if not args.no_secondary:
+        for key in SECONDARY:
+            if key == args.workload:
+                continue
+            sw = inputs.WORKLOADS[key]
+            secondary[sw.name] = run_secondary(sw, reps=max(20, args.steps),
+                                               warmup=max(5, args.warmup))
 
     split = None
     if not args.no_secondary and w.N % 4 == 0:
@@ -478,15 +685,21 @@ def main():
                    "causal": w.causal, "passes": "fwd+bwd" if w.backward else "fwd",
                    "flops_per_step": f + b},
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "step_ms": {"mean": ms, "median": med, "min": mn, "steps": len(per_step),
+                    "tflops_median": (f + b) / med / 1e9, "tflops_min_time": (f + b) / mn / 1e9},
+        "sclk": clk,
+        "pct_of_bf16_peak_at_measured_clock": (
+            100.0 * value / (PEAK_BF16_TFLOPS * clk["mean_mhz"] / NOMINAL_SCLK_MHZ)
+            if clk else None),
         "passes": passes,
         "kernels": kernels,
-        "roofline": {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak,
-                     "unit": unit, "frac": achieved / peak,
-                     "traffic": profiled_traffic(w.name, dom)},
+        "kernel_timing_pass": {"steps": max(args.steps, 3), "ms_per_step": kernel_pass_ms,
+                               "note": "per-kernel events on; separate from the headline steps"},
+        "roofline": roofline,
         "cpu_baseline": cpu,
     }
     if secondary:
-        out["fwd_n16384_d128"] = secondary
+        out["secondary"] = secondary
     if split:
         out["split_fwd"] = split
     print(json.dumps(out), flush=True)

@@ -15,8 +15,13 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_merge.hip", "fa_timing.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_d128.hip", "fa_merge.hip",
+           "fa_timing.hip"]
 ARCH = "gfx950"
+# Extra flags per source.  fa_bwd_d128.hip: MFMA results in VGPRs (the
+# unmasked D = 128 dK/dV kernel otherwise moves its accumulators between
+# register files on every tile).
+EXTRA_FLAGS = {"fa_bwd_d128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc():
@@ -51,7 +56,8 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *compile_flags(), *EXTRA_FLAGS.get(src, []), "-c",
+                     os.path.join(CSRC, src), "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()

@@ -49,6 +49,8 @@ hipError_t launch_merge(const MergeArgs& a);
 hipError_t launch_bwd_delta(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);
+// dK/dV at D = 128 without a mask (fa_bwd_d128.hip, its own compile flags).
+hipError_t launch_bwd_dkdv_d128_nomask(const BwdArgs& a);
 
 // Optional per-kernel event timing (fa_timing.cpp).  No-ops when disabled.
 struct TimedLaunch {

@@ -59,6 +59,14 @@ WORKLOADS = {
     # Scale test of the linear-memory claim: a 128K-token causal training step.
     "n128k": Workload("train_causal_bf16_b1h8n131072d64", 6, 1, 8, 131072, 64, "bf16", True, True,
                       check_rows=64),
+    # D = 128 forwards at the short end of the N >= 4096 range (the N = 16384
+    # recipe, inputs x 0.5) and a D = 128 training step.
+    "n4k_d128": Workload("fwd_bf16_b1h16n4096d128_x0.5", 8, 1, 16, 4096, 128, "bf16", False,
+                         False, input_mult=0.5, check_rows=128),
+    "n8k_d128": Workload("fwd_bf16_b1h16n8192d128_x0.5", 9, 1, 16, 8192, 128, "bf16", False,
+                         False, input_mult=0.5, check_rows=128),
+    "train_d128": Workload("train_bf16_b1h16n16384d128", 10, 1, 16, 16384, 128, "bf16", False,
+                           True, check_rows=64),
 }
 
 
