@@ -387,3 +387,37 @@ def test_workload_n128k_causal_training_subset():
     say(f"    {len(krows)} key rows: dK={ek:.2e} dV={ev:.2e}")
     assert ok and el <= 1e-3 and eq <= 5e-2
     assert ek <= 5e-2 and ev <= 5e-2
+
+
+def test_workload_d128_training_subset():
+    """The D = 128 training step (B=1, H=16, N=16384, no mask; the unmasked
+    D = 128 dK/dV kernel has its own build unit): seeded query rows (O, LSE,
+    dQ) and key rows of the first and last head (dK, dV) against the
+    oracle."""
+    w = inputs.WORKLOADS["train_d128"]
+    say(f"[{w.name}]")
+    vals, devs = _workload_devs(w)
+    o, lse = _fwd(devs, w.scale, w.causal)
+    dq, dk, dv = fa.backward(devs["q"], devs["k"], devs["v"], o, devs["do"], lse, w.scale,
+                             w.causal)
+    torch.cuda.synchronize()
+    qrows = inputs.check_row_subset(w)
+    ro, rl = oracle.attention_fwd_rows(vals["q"], vals["k"], vals["v"], w.scale, w.causal, qrows)
+    rq = oracle.attention_bwd_query_rows(vals["q"], vals["k"], vals["v"], vals["do"], w.scale,
+                                         w.causal, qrows)
+    eo, er, ok = o_ok(_sampled(o, qrows), ro, "bf16")
+    el = max_abs(to_f64(lse)[tuple(qrows.T)], rl)
+    eq = rel_to_max(_sampled(dq, qrows), rq)
+    say(f"    {len(qrows)} query rows: O={eo:.2e} (rel-to-max {er:.2e}) LSE={el:.2e} dQ={eq:.2e}")
+    krows = _key_rows_two_heads(w, count=64)
+    stats = {}
+    for h in sorted({int(r[1]) for r in krows}):
+        say(f"    oracle row statistics of head {h} ...")
+        stats[(0, h)] = oracle.row_stats(vals["q"], vals["k"], vals["v"], vals["do"], w.scale,
+                                         w.causal, 0, h, block_rows=1024)
+    rk, rv = oracle.attention_bwd_key_rows(vals["q"], vals["k"], vals["v"], vals["do"], w.scale,
+                                           w.causal, krows, stats=stats)
+    ek, ev = rel_to_max(_sampled(dk, krows), rk), rel_to_max(_sampled(dv, krows), rv)
+    say(f"    {len(krows)} key rows: dK={ek:.2e} dV={ev:.2e}")
+    assert ok and el <= 1e-3 and eq <= 5e-2
+    assert ek <= 5e-2 and ev <= 5e-2
