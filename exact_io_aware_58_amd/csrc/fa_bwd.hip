@@ -103,7 +103,8 @@ __global__ void __launch_bounds__(256, 2)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ nlse, const float* __restrict__ ndelta,
-              uint16_t* __restrict__ dQ, int N, float c, float scale, int nqt, int total) {
+              uint16_t* __restrict__ dQ, int N, float c, float scale, int nqt, int total,
+              int tile_major) {
   constexpr int BC = DqTile<D>::BC;
   constexpr int TILE = BC * D;             // elements of one K or V tile
   constexpr int BLOCKS = TILE * 2 / 1024;  // 1 KiB blocks per tile
@@ -121,10 +122,9 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int l32 = lane & 31, hh = lane >> 5;
 
-  const int logical = xcd_logical_block(blockIdx.x, total);
-  const int bh = logical / nqt;
-  int qt = logical - bh * nqt;
-  if (CAUSAL) qt = nqt - 1 - qt;
+  int bh, qt;
+  tile_of(blockIdx.x, total, nqt, tile_major, bh, qt);
+  if (CAUSAL) qt = nqt - 1 - qt;  // longest rows first
   const int q0 = qt * kDqBR;
   const int wq0 = q0 + wave * 32;
   const int myq = wq0 + l32;
@@ -334,7 +334,7 @@ static hipError_t dq(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
                      (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                      (const uint16_t*)a.dO, a.nlse, a.ndelta, (uint16_t*)a.dQ, a.N,
-                     a.scale * kLog2e, a.scale, nqt, total);
+                     a.scale * kLog2e, a.scale, nqt, total, tile_major(CAUSAL, nqt, total));
   return hipGetLastError();
 }
 

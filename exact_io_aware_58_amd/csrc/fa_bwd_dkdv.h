@@ -35,7 +35,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ nlse, const float* __restrict__ ndelta,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, float c,
-                float scale, int nkt, int total) {
+                float scale, int nkt, int total, int tile_major) {
   constexpr int BR = DkvTile<D>::BR;
   constexpr int TILE = BR * D;                  // elements of one Q or dO tile
   constexpr int BLOCKS = TILE * 2 / 1024;       // 1 KiB blocks per tile
@@ -54,9 +54,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int l32 = lane & 31, hh = lane >> 5;
 
-  const int logical = xcd_logical_block(blockIdx.x, total);
-  const int bh = logical / nkt;
-  const int kt = logical - bh * nkt;  // causal: small kt has the most queries, runs first
+  int bh, kt;  // causal: small kt has the most queries, runs first
+  tile_of(blockIdx.x, total, nkt, tile_major, bh, kt);
   const int k0 = kt * kDkvKeys;
   const int wk0 = k0 + wave_u * 32;
   const int mykey = wk0 + l32;
@@ -276,7 +275,7 @@ static hipError_t dkdv(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
                      (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                      (const uint16_t*)a.dO, a.nlse, a.ndelta, (uint16_t*)a.dK, (uint16_t*)a.dV,
-                     a.N, a.scale * kLog2e, a.scale, nkt, total);
+                     a.N, a.scale * kLog2e, a.scale, nkt, total, tile_major(CAUSAL, nkt, total));
   return hipGetLastError();
 }
 

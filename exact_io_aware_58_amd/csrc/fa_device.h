@@ -281,4 +281,25 @@ __device__ inline int xcd_logical_block(int pid, int total) {
   return x * q + (x < r ? x : r) + local;
 }
 
+// (batch*head, tile) of workgroup `pid` in a grid of `total` = heads x
+// `ntile` workgroups.  Head-major (the default) goes through
+// xcd_logical_block, so a head's tiles share one XCD's L2.  Tile-major puts
+// the tile index outermost: consecutive workgroups are the same tile of
+// different heads, and since workgroups are dealt to the XCDs in dispatch
+// order, every tile rank is spread over all XCDs.  Causal grids with few
+// tiles per head but several rounds of workgroups use it so that the
+// longest tiles of all heads run first (head-major would interleave long
+// and short ones).
+__device__ inline void tile_of(int pid, int total, int ntile, int tile_major, int& bh, int& t) {
+  if (tile_major) {
+    const int nbh = total / ntile;
+    t = pid / nbh;
+    bh = pid - t * nbh;
+  } else {
+    const int logical = xcd_logical_block(pid, total);
+    bh = logical / ntile;
+    t = logical - bh * ntile;
+  }
+}
+
 }  // namespace fa

@@ -167,7 +167,7 @@ __global__ void __launch_bounds__(256, 2)
 fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
              const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
              float* __restrict__ LSE, int Nq, int Nk, int dlt, float c, int nqt,
-             int total) {
+             int total, int tile_major) {
   constexpr int BC = FwdTile<D>::BC;
   constexpr int TILE = BC * D;             // elements of one K or V tile
   constexpr int BLOCKS = TILE * 2 / 1024;  // 1 KiB blocks per tile
@@ -189,9 +189,8 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int l32 = lane & 31, hh = lane >> 5;
 
-  const int logical = xcd_logical_block(blockIdx.x, total);
-  const int bh = logical / nqt;
-  int qt = logical - bh * nqt;
+  int bh, qt;
+  tile_of(blockIdx.x, total, nqt, tile_major, bh, qt);
   if (CAUSAL) qt = nqt - 1 - qt;  // longest rows first
   const int q0 = qt * kFwdBR;
   const int wq0 = q0 + wave * 32;
@@ -363,7 +362,6 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // Group B, which is in its softmax phase whenever loads are issued, issues
 // all of them, so the MFMA-phase waves start on their operands at once.
 constexpr int kPpBR = 256;
-constexpr int kCUs = 256;  // compute units of an MI355X
 
 template <typename T, int D, bool CAUSAL, int GROUP>
 __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
@@ -371,7 +369,7 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
                                              const uint16_t* __restrict__ V,
                                              uint16_t* __restrict__ O, float* __restrict__ LSE,
                                              int Nq, int Nk, int dlt, float c, int nqt,
-                                             int total, uint16_t* kb0,
+                                             int total, int tile_major, uint16_t* kb0,
                                              uint16_t* kb1, uint16_t* vb0, uint16_t* vb1) {
   constexpr int BC = FwdTile<D>::BC;
   constexpr int TILE = BC * D;
@@ -387,9 +385,8 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int l32 = lane & 31, hh = lane >> 5;
 
-  const int logical = xcd_logical_block(blockIdx.x, total);
-  const int bh = logical / nqt;
-  int qt = logical - bh * nqt;
+  int bh, qt;
+  tile_of(blockIdx.x, total, nqt, tile_major, bh, qt);
   if (CAUSAL) qt = nqt - 1 - qt;  // longest rows first
   const int q0 = qt * kPpBR;
   const int wq0 = q0 + wave * 32;
@@ -547,7 +544,7 @@ __global__ void __launch_bounds__(512, 1)
 fwd16pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                float* __restrict__ LSE, int Nq, int Nk, int dlt, float c, int nqt,
-               int total) {
+               int total, int tile_major) {
   constexpr int TILE = FwdTile<D>::BC * D;
   // Separate buffers with compile-time selection (the slot loop is unrolled
   // over two tiles): loads into one buffer never alias reads of another.
@@ -557,11 +554,11 @@ fwd16pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   __shared__ __attribute__((aligned(1024))) uint16_t vb1[TILE];
   // Each group runs its own copy of the slot loop (no per-slot branch on it).
   if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 8) == 0)
-    fwd16pp_body<T, D, CAUSAL, 0>(Q, K, V, O, LSE, Nq, Nk, dlt, c, nqt, total, kb0, kb1, vb0,
-                                  vb1);
+    fwd16pp_body<T, D, CAUSAL, 0>(Q, K, V, O, LSE, Nq, Nk, dlt, c, nqt, total, tile_major, kb0,
+                                  kb1, vb0, vb1);
   else
-    fwd16pp_body<T, D, CAUSAL, 1>(Q, K, V, O, LSE, Nq, Nk, dlt, c, nqt, total, kb0, kb1, vb0,
-                                  vb1);
+    fwd16pp_body<T, D, CAUSAL, 1>(Q, K, V, O, LSE, Nq, Nk, dlt, c, nqt, total, tile_major, kb0,
+                                  kb1, vb0, vb1);
 }
 
 // fp32 kernel: true fp32 products on the vector ALUs (no reduced-precision
@@ -660,19 +657,21 @@ static hipError_t launch16(const FwdArgs& a) {
   // whose finer granularity evens out a partial last round.
   const int npp = (a.Nq + kPpBR - 1) / kPpBR;
   const long wpp = (long)npp * a.B * a.H;
-  if (wpp >= 2 * kCUs || wpp % kCUs == 0) {
+  const int cus = cu_count();
+  if (wpp >= 2L * cus || wpp % cus == 0) {
     const int total = npp * a.B * a.H;
     hipLaunchKernelGGL((fwd16pp_kernel<T, D, CAUSAL>), dim3(total), dim3(512), 0, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                        (uint16_t*)a.O, a.LSE, a.Nq, a.Nk, a.delta, a.scale * kLog2e, npp,
-                       total);
+                       total, tile_major(CAUSAL, npp, total));
     return hipGetLastError();
   }
   const int nqt = (a.Nq + kFwdBR - 1) / kFwdBR;
   const int total = nqt * a.B * a.H;
   hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL>), dim3(total), dim3(256), 0, a.stream,
                      (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                     (uint16_t*)a.O, a.LSE, a.Nq, a.Nk, a.delta, a.scale * kLog2e, nqt, total);
+                     (uint16_t*)a.O, a.LSE, a.Nq, a.Nk, a.delta, a.scale * kLog2e, nqt, total,
+                     tile_major(CAUSAL, nqt, total));
   return hipGetLastError();
 }
 
