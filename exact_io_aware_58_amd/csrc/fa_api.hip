@@ -57,12 +57,17 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 
-// Device address of this device's scratch (the current device, which must be
-// the one the caller's stream belongs to); looked up on the first call on a
-// device.
-int device_scratch(void** out) {
+// Device address of the current device's scratch, looked up on the first
+// call on that device.  The caller's stream must belong to the current
+// device (the lookup and the kernels must agree on the GPU).
+int device_scratch(hipStream_t stream, void** out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return FA_ERR_HIP;
+    if (sdev != dev) return FA_ERR_INVALID_ARG;
+  }
   std::lock_guard<std::mutex> g(g_scratch_mu);
   if (!g_scratch_ptr[dev]) {
     void* p = nullptr;
@@ -219,7 +224,7 @@ extern "C" int fa_bwd_noalloc(int dtype, int B, int H, int N, int D, float scale
   const size_t rows_bytes = delta_bytes(B, H, N);
   if (2 * rows_bytes > kScratchBytes) return FA_ERR_WORKSPACE;
   void* base = nullptr;
-  rc = device_scratch(&base);
+  rc = device_scratch((hipStream_t)stream, &base);
   if (rc != FA_OK) return rc;
   // Every element the kernels read from the scratch is written first by the
   // Delta kernel of this same call, so nothing needs clearing.

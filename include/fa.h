@@ -169,10 +169,11 @@ int fa_bwd(int dtype, int B, int H, int N, int D, float scale, int causal,
  * Allocates, frees and synchronises nothing.
  *
  *   Arguments as fa_bwd, without workspace and workspace_bytes.  The stream
- *   must belong to the current device (the one whose scratch is used).
- *   Returns FA_ERR_WORKSPACE if fa_bwd_workspace_bytes(...) for the problem
- *   exceeds fa_bwd_noalloc_max_bytes() (B * H * N above 2^22 rows), and
- *   FA_ERR_HIP if the scratch's device address cannot be looked up.
+ *   must belong to the current device (the one whose scratch is used):
+ *   FA_ERR_INVALID_ARG otherwise.  Returns FA_ERR_WORKSPACE if
+ *   fa_bwd_workspace_bytes(...) for the problem exceeds
+ *   fa_bwd_noalloc_max_bytes() (B * H * N above 2^22 rows), and FA_ERR_HIP
+ *   if the stream's device or the scratch's address cannot be looked up.
  *   All calls on one GPU share its scratch: calls that overlap in time on
  *   one GPU (several streams or threads) race and must be serialised by the
  *   caller.  The scratch keeps the last call's row statistics; every value a
