@@ -11,6 +11,13 @@ kernel's error, not input quantisation.
 Recipe: workload k uses seed k; tensor t in {Q: 0, K: 1, V: 2, dO: 3} is
 numpy.random.default_rng([k, t]).standard_normal(shape, dtype=float32),
 times the workload's input multiplier, then rounded to the dtype.
+
+Grid recipe (draw_grid), for sizes where normal variates and their rounding
+take tens of seconds per tensor (a 2^23 x 128 head): each element is
+(2u - 31) / 16 with u = one byte of numpy.random.default_rng([k, t, 1]).bytes
+masked to 0..31, i.e. 32 equally likely levels in [-1.9375, 1.9375], mean 0,
+variance 1.33.  Every level is exact in bf16, fp16 and f32, so the values
+need no rounding and sums of them are exact in float64.
 """
 from __future__ import annotations
 
@@ -104,6 +111,23 @@ def draw(seed: int, tensor: str, shape, dtype: str, mult: float = 1.0):
     if mult != 1.0:
         x = x * np.float32(mult)
     return round_to_dtype(x, dtype)
+
+
+def draw_grid(seed: int, tensor: str, shape, dtype: str):
+    """One seeded grid-valued tensor (see the module docstring):
+    (float32 values, raw storage array)."""
+    rng = np.random.default_rng([seed, TENSOR_IDS[tensor], 1])
+    u = np.frombuffer(rng.bytes(int(np.prod(shape))), dtype=np.uint8).reshape(shape)
+    x = (u & 31).astype(np.float32)
+    x *= np.float32(2.0 / 16.0)
+    x -= np.float32(31.0 / 16.0)
+    if dtype == "bf16":
+        return x, (x.view(np.uint32) >> 16).astype(np.uint16)  # exact: low half is zero
+    if dtype == "f16":
+        return x, x.astype(np.float16)
+    if dtype == "f32":
+        return x, x
+    raise ValueError(f"unknown dtype {dtype!r}")
 
 
 def make_inputs(w: Workload, with_grad=None):

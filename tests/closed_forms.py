@@ -90,6 +90,34 @@ def uniform_backward(k, v, do, scale, causal, block=256):
     return dq, dk, dv
 
 
+def causal_uniform_forward_ranges(v, ranges):
+    """Causal O at Q = 0 (prefix means of V) on row ranges [(r0, r1), ...] of
+    one head v (N, D), without the whole prefix-sum array: each range starts
+    from one sum of the rows before it.  Returns float64 (rows, D), the
+    ranges' rows in order."""
+    v = np.asarray(v)
+    out = []
+    for r0, r1 in ranges:
+        start = np.add.reduce(v[:r0], axis=0, dtype=np.float64) if r0 else 0.0
+        s = start + np.cumsum(v[r0:r1], axis=0, dtype=np.float64)
+        out.append(s / np.arange(r0 + 1, r1 + 1, dtype=np.float64)[:, None])
+    return np.concatenate(out)
+
+
+def causal_uniform_dv_ranges(do, ranges):
+    """Causal dV at Q = 0, dV_j = sum_{i >= j} dO_i / (i + 1), on row ranges
+    of one head do (N, D) (float64 for the weighted sum of the rows after each
+    range).  Returns float64 (rows, D)."""
+    do = np.asarray(do)
+    N = do.shape[0]
+    out = []
+    for r0, r1 in ranges:
+        after = (1.0 / np.arange(r1 + 1, N + 1, dtype=np.float64)) @ do[r1:] if r1 < N else 0.0
+        inner = do[r0:r1] / np.arange(r0 + 1, r1 + 1, dtype=np.float64)[:, None]
+        out.append(after + np.cumsum(inner[::-1], axis=0)[::-1])
+    return np.concatenate(out)
+
+
 def within(got, ref, rel, slack):
     """Largest |got - ref| / (rel * |ref| + slack) over all elements: <= 1
     means every element lies within `rel` of its reference (relative) plus

@@ -10,7 +10,10 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.closed_forms import BF16_HALF_ULP_REL, uniform_backward, uniform_forward, within
+from exact_io_aware_58_amd import inputs
+from tests.closed_forms import (BF16_HALF_ULP_REL, causal_uniform_dv_ranges,
+                                causal_uniform_forward_ranges, uniform_backward,
+                                uniform_forward, within)
 from tests.gpu_util import TOL, o_ok, rel_to_max
 
 
@@ -85,3 +88,31 @@ def test_o_check_rejects_zero_output_where_max_abs_alone_would_pass():
     off[i] += 0.03 * np.max(np.abs(ref))   # 3% of the largest output
     assert not o_ok(off, ref, "bf16")[2]
     assert rel_to_max(off, ref) > TOL["bf16"]["o_rel"]
+
+
+@pytest.mark.parametrize("ranges", [[(0, 37)], [(0, 5), (20, 37)], [(3, 4), (36, 37)], [(10, 30)]])
+def test_uniform_ranges_match_the_full_closed_forms(ranges):
+    """The row-range forms used at N = 2^23 equal the whole-array closed forms
+    (pinned to the oracle above) on the same rows."""
+    N, D = 37, 6
+    v, do = _rand((1, 1, N, D), 6), _rand((1, 1, N, D), 7)
+    o, _ = uniform_forward(v, True)
+    _, _, dv = uniform_backward(_rand((1, 1, N, D), 8), v, do, 0.7, True)
+    rows = np.concatenate([np.arange(r0, r1) for r0, r1 in ranges])
+    assert np.max(np.abs(causal_uniform_forward_ranges(v[0, 0], ranges) - o[0, 0, rows])) <= 1e-12
+    assert np.max(np.abs(causal_uniform_dv_ranges(do[0, 0], ranges) - dv[0, 0, rows])) <= 1e-12
+
+
+def test_grid_inputs_are_exact_and_balanced():
+    """draw_grid: 32 levels (2u - 31)/16, each exact in bf16 and fp16 (the raw
+    storage decodes to the same value), mean ~0, variance ~1.33, and a
+    different stream per tensor."""
+    x, raw = inputs.draw_grid(3, "k", (4, 4096), "bf16")
+    assert np.array_equal(inputs.bf16_bits_to_f32(raw), x)
+    levels = np.unique(x)
+    assert np.array_equal(levels, (2 * np.arange(32) - 31) / 16)
+    assert abs(float(x.mean())) < 0.02 and abs(float(x.var()) - 341 / 256) < 0.03
+    xh, rawh = inputs.draw_grid(3, "k", (4, 4096), "f16")
+    assert np.array_equal(xh, x) and np.array_equal(rawh.astype(np.float32), x)
+    xv, _ = inputs.draw_grid(3, "v", (4, 4096), "bf16")
+    assert not np.array_equal(xv, x)
