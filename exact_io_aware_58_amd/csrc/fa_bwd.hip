@@ -136,6 +136,23 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const i32x4 rK = rsrc_words(K + base, head_bytes);  // direct-to-LDS sources
   const i32x4 rV = rsrc_words(V + base, head_bytes);
 
+  const int kend = CAUSAL ? min(N, q0 + kDqBR) : N;
+  const int ntiles = (kend + BC - 1) / BC;
+
+  auto dma = [&](const uint16_t* S0, int ts) {
+#pragma unroll
+    for (int i = 0; i < BLOCKS / 4; ++i) {
+      const int b = wave_u + 4 * i;
+      const uint32_t goff = dma_goff<D>(b, lane, ts);
+      lds_dma16(rK, S0 + b * 512, goff);
+      lds_dma16(rV, S0 + TILE + b * 512, goff);
+    }
+  };
+
+  const int nfull = min(N / BC, CAUSAL ? (q0 + 1) / BC : ntiles);
+  // The first key tile travels while Q and dO load.
+  if (nfull > 0) dma(smem0, 0);
+
   u32x4 qf[NDC], gf[NDC];
 #pragma unroll
   for (int cc = 0; cc < NDC; ++cc) {
@@ -173,19 +190,6 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int t = 0; t < 2; ++t)
       toffs[db][t] = toff<D>(8 * t + 4 * (G >> 1) + (a16 >> 2), 32 * db + 16 * (G & 1) + 4 * (a16 & 3));
-
-  const int kend = CAUSAL ? min(N, q0 + kDqBR) : N;
-  const int ntiles = (kend + BC - 1) / BC;
-
-  auto dma = [&](const uint16_t* S0, int ts) {
-#pragma unroll
-    for (int i = 0; i < BLOCKS / 4; ++i) {
-      const int b = wave_u + 4 * i;
-      const uint32_t goff = dma_goff<D>(b, lane, ts);
-      lds_dma16(rK, S0 + b * 512, goff);
-      lds_dma16(rV, S0 + TILE + b * 512, goff);
-    }
-  };
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -251,9 +255,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // Tiles wholly visible to every row of the workgroup (no tail, not past
   // the causal diagonal) run the straight-line body, double-buffered; the
   // remaining ones (at the end) the masked body, unpipelined.
-  const int nfull = min(N / BC, CAUSAL ? (q0 + 1) / BC : ntiles);
   int t = 0;
-  if (nfull > 0) dma(smem0, 0);
   wait_dma();
   __syncthreads();
   for (; t < nfull; t += 2) {

@@ -69,6 +69,29 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const auto rK = make_rsrc(K + base, head_bytes);
   const auto rV = make_rsrc(V + base, head_bytes);
 
+  const int qstart = CAUSAL ? k0 : 0;  // earlier queries see none of these keys
+  const int ntiles = qstart < N ? (N - qstart + BR - 1) / BR : 0;
+
+  // Direct global->LDS loads of one query tile: each wave two blocks of Q and
+  // two of dO; wave 0 also 64 -LSE/scale values, wave 1 64 -Delta values.
+  // Rows past N arrive as zeros (then P = 1 but dO = Q = 0: no contribution).
+  auto dma = [&](const uint16_t* S0, int qs) {
+#pragma unroll
+    for (int i = 0; i < BLOCKS / 4; ++i) {
+      const int b = wave_u + 4 * i;
+      const uint32_t goff = dma_goff<D>(b, lane, qs);
+      lds_dma16(rQ, S0 + b * 512, goff);
+      lds_dma16(rdO, S0 + TILE + b * 512, goff);
+    }
+    if (wave_u == 0)
+      lds_dma4(rL, S0 + 2 * TILE, (uint32_t)(qs + lane) * 4u);
+    else if (wave_u == 1)
+      lds_dma4(rD, S0 + 2 * TILE + 128, (uint32_t)(qs + lane) * 4u);
+  };
+
+  // The first query tile travels while K and V load.
+  if (ntiles > 0) dma(smem0, qstart);
+
   // B operands of S = Q K^T and dP = dO V^T: lane holds row `mykey` of K, V.
   u32x4 kf[NDC], vf[NDC];
 #pragma unroll
@@ -96,26 +119,6 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int t = 0; t < 2; ++t)
       toffs[db][t] = toff<D>(8 * t + 4 * (G >> 1) + (a16 >> 2), 32 * db + 16 * (G & 1) + 4 * (a16 & 3));
-
-  const int qstart = CAUSAL ? k0 : 0;  // earlier queries see none of these keys
-  const int ntiles = qstart < N ? (N - qstart + BR - 1) / BR : 0;
-
-  // Direct global->LDS loads of one query tile: each wave two blocks of Q and
-  // two of dO; wave 0 also 64 -LSE/scale values, wave 1 64 -Delta values.
-  // Rows past N arrive as zeros (then P = 1 but dO = Q = 0: no contribution).
-  auto dma = [&](const uint16_t* S0, int qs) {
-#pragma unroll
-    for (int i = 0; i < BLOCKS / 4; ++i) {
-      const int b = wave_u + 4 * i;
-      const uint32_t goff = dma_goff<D>(b, lane, qs);
-      lds_dma16(rQ, S0 + b * 512, goff);
-      lds_dma16(rdO, S0 + TILE + b * 512, goff);
-    }
-    if (wave_u == 0)
-      lds_dma4(rL, S0 + 2 * TILE, (uint32_t)(qs + lane) * 4u);
-    else if (wave_u == 1)
-      lds_dma4(rD, S0 + 2 * TILE + 128, (uint32_t)(qs + lane) * 4u);
-  };
 
   f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
@@ -212,13 +215,13 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   int t = 0;
   const int ndiag = CAUSAL ? min(ntiles, kDkvKeys / BR) : 0;
   for (; t < ndiag; ++t) {
-    dma(smem0, qstart + t * BR);
+    if (t > 0) dma(smem0, qstart + t * BR);
     wait_dma();
     __syncthreads();
     tile(smem0, qstart + t * BR, std::true_type());
     __syncthreads();
   }
-  if (t < ntiles) dma(smem0, qstart + t * BR);
+  if (t > 0 && t < ntiles) dma(smem0, qstart + t * BR);
   wait_dma();
   __syncthreads();
   if constexpr (D == 128 && !CAUSAL) {

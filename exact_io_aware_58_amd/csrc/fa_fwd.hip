@@ -399,6 +399,17 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
   const i32x4 rK = rsrc_words(K + kbase, kv_bytes);  // direct-to-LDS sources
   const i32x4 rV = rsrc_words(V + kbase, kv_bytes);
 
+  // Loads of one tile, issued by the four waves of group B only.
+  auto dma_tile = [&](const uint16_t* dst, const i32x4& r, int ts) {
+#pragma unroll
+    for (int i = 0; i < BLOCKS / 4; ++i) {
+      const int b = (wave_u - 4) + 4 * i;
+      lds_dma16(r, dst + b * 512, dma_goff<D>(b, lane, ts));
+    }
+  };
+  // K of tile 0 travels while the queries load (one memory latency, not two).
+  if (GROUP != 0) dma_tile(kb0, rK, 0);
+
   u32x4 qf[NDC];
 #pragma unroll
   for (int cc = 0; cc < NDC; ++cc)
@@ -420,15 +431,6 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
 
   const int kend = CAUSAL ? max(0, min(Nk, q0 + kPpBR + dlt)) : Nk;
   const int ntiles = (kend + BC - 1) / BC;
-
-  // Loads of one tile, issued by the four waves of group B only.
-  auto dma_tile = [&](const uint16_t* dst, const i32x4& r, int ts) {
-#pragma unroll
-    for (int i = 0; i < BLOCKS / 4; ++i) {
-      const int b = (wave_u - 4) + 4 * i;
-      lds_dma16(r, dst + b * 512, dma_goff<D>(b, lane, ts));
-    }
-  };
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -503,7 +505,6 @@ __device__ __forceinline__ void fwd16pp_body(const uint16_t* __restrict__ Q,
   // K of tile j+1 and V of tile j are loaded at slot 2j (two buffers each)
   // and first read at slot 2j+2; the odd slots' barriers wait for them.
   constexpr bool A = GROUP == 0;
-  if (!A) dma_tile(kb0, rK, 0);
   barrier_after_loads();
   // Slots 2t .. 2t+3 cover tiles t and t+1; group B runs one slot behind.
   for (int t = 0; t <= ntiles; t += 2) {
