@@ -199,13 +199,16 @@ def run_gpu(w, steps, warmup, clock=None, clock_window_s=3.5):
     return total_ms / steps, per_step, kernels, timed_ms, clk
 
 
-def run_secondary(w, reps=20, warmup=5):
-    """One workload timed launch by launch: `warmup` untimed passes, then
-    `reps` launches of fa_fwd (and, with a backward, `reps` of fa_bwd after
-    them), each between the events recorded before and after it on the
-    launch stream (mean, median, minimum), then `reps` more between two
-    events only (``batch_ms``: short kernels lose a few microseconds to the
-    events between launches).
+def run_secondary(w, reps=20, warmup=5, warmup_s=0.05, min_timed_s=0.1):
+    """One workload timed launch by launch, per pass (fa_fwd; with a
+    backward, fa_bwd after it): untimed launches until at least `warmup` of
+    them and `warmup_s` seconds have run (the first tens of milliseconds of a
+    burst run while the shader clock is still moving: at N = 8192, D = 128
+    the first ~25 ms of launches take ~3% longer than the settled ones), then
+    at least `reps` launches and `min_timed_s` seconds, each between the
+    events recorded before and after it on the launch stream (mean, median,
+    minimum), then as many more between two events only (``batch_ms``: short
+    kernels lose a few microseconds to the events between launches).
     Returns a dict with mean, median and minimum per pass and the rates."""
     import statistics
 
@@ -228,31 +231,45 @@ def run_secondary(w, reps=20, warmup=5):
             raise fa.FAError(rc, "fa_fwd")
 
     def timed(fn):
+        # warm-up by count and by time; its last chunk also sizes the timed
+        # series (at least `reps` launches and `min_timed_s` seconds)
+        done, t0, chunk = 0, time.perf_counter(), max(1, warmup)
+        while True:
+            c0 = time.perf_counter()
+            for _ in range(chunk):
+                fn()
+            torch.cuda.synchronize()
+            done += chunk
+            per_launch = (time.perf_counter() - c0) / chunk
+            if done >= warmup and time.perf_counter() - t0 >= warmup_s:
+                break
+            chunk = max(1, min(1000, int(0.01 / max(per_launch, 1e-7))))
+        n = max(reps, min(5000, int(min_timed_s / max(per_launch, 1e-7)) + 1))
         # launches enqueued back to back with one event between consecutive
         # launches, so the GPU's queue never waits for the host; then the
         # same number of launches between just two events (no event work
         # between kernels: the rate the kernels sustain when queued)
-        for _ in range(warmup):
-            fn()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
         ev[0].record(stream)
-        for i in range(reps):
+        for i in range(n):
             fn()
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(reps):
+        for _ in range(n):
             fn()
         e1.record(stream)
         torch.cuda.synchronize()
-        return per, e0.elapsed_time(e1) / reps
+        counts.append((done, n))
+        return per, e0.elapsed_time(e1) / n
 
     f, b = flops(w)
     out = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "dtype": w.dtype,
-           "causal": w.causal, "input_mult": w.input_mult, "launches": reps, "warmup": warmup}
+           "causal": w.causal, "input_mult": w.input_mult, "min_launches": reps,
+           "min_warmup_launches": warmup, "min_warmup_s": warmup_s, "min_timed_s": min_timed_s}
+    counts = []  # (warm-up launches, timed launches) per pass
 
     def summary(res, work):
         t, batch = res
@@ -282,6 +299,9 @@ def run_secondary(w, reps=20, warmup=5):
 
         out["bwd"] = summary(timed(bwd), b)
         del dq, dk, dv, ws
+    out["fwd"]["warmup_launches"], out["fwd"]["launches"] = counts[0]
+    if w.backward:
+        out["bwd"]["warmup_launches"], out["bwd"]["launches"] = counts[1]
     log(f"[bench] {w.name}: fwd median {out['fwd']['median_ms']:.4f} ms"
         + (f", bwd median {out['bwd']['median_ms']:.4f} ms" if w.backward else ""))
     del devs, q, k, v, o, lse
