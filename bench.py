@@ -439,6 +439,49 @@ def cpu_baseline(w, rows):
     }
 
 
+def three_kernel_forward(q, k, v, scale):
+    """The unfused attention forward in PyTorch on the same GPU: scores and
+    probabilities materialised in HBM between a matmul, a softmax and a
+    matmul (plus the copy that makes K^T contiguous and the scaling)."""
+    import torch
+    s_ = torch.matmul(q, k.transpose(-2, -1).contiguous()) * scale
+    p_ = torch.softmax(s_, dim=-1)
+    return torch.matmul(p_, v)
+
+
+def run_io(ns, heads=16, D=64, passes=2):
+    """HBM bytes of one forward pass, fused against the three-kernel path,
+    for counting under `rocprofv3 --pmc FETCH_SIZE` (then `WRITE_SIZE`): per
+    N, once the inputs are resident, `passes` times the fused forward and then
+    the three-kernel forward, each followed by a synchronisation, and nothing
+    else on the GPU in between.  B = 1, bf16, no mask.  Prints one JSON line
+    per N with the kernels' wall times (each pass timed alone)."""
+    import torch
+    from exact_io_aware_58_amd import fa, inputs
+
+    scale = 1.0 / D ** 0.5
+    for N in ns:
+        w = inputs.Workload(f"io_n{N}", 7, 1, heads, N, D, "bf16", False, False)
+        devs = {n: upload(raw, "bf16") for n, (_, raw) in inputs.make_inputs(w).items()}
+        q, k, v = devs["q"], devs["k"], devs["v"]
+        torch.cuda.synchronize()
+        row = {"N": N, "B": 1, "H": heads, "D": D, "causal": False, "passes": passes,
+               "fused_ms": [], "three_kernel_ms": []}
+        for _ in range(passes):
+            for key, fn in (("fused_ms", lambda: fa.forward(q, k, v, scale, False)),
+                            ("three_kernel_ms", lambda: three_kernel_forward(q, k, v, scale))):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                out = fn()
+                e1.record()
+                torch.cuda.synchronize()
+                row[key].append(e0.elapsed_time(e1))
+                del out
+        print(json.dumps(row), flush=True)
+        del q, k, v, devs
+        torch.cuda.empty_cache()
+
+
 def run_sweep(ns, heads=16, D=64, reps=5):
     """Sequence-length sweep (one JSON line per N): forward and backward time
     and device memory of this library beside the three-kernel PyTorch path
@@ -484,9 +527,7 @@ def run_sweep(ns, heads=16, D=64, reps=5):
         del dq, dk, dv, ws
 
         def naive():
-            s_ = torch.matmul(q, k.transpose(-2, -1).contiguous()) * scale
-            p_ = torch.softmax(s_, dim=-1)
-            return torch.matmul(p_, v)
+            return three_kernel_forward(q, k, v, scale)
 
         try:
             torch.cuda.synchronize()
@@ -505,6 +546,20 @@ def run_sweep(ns, heads=16, D=64, reps=5):
         print(json.dumps(row), flush=True)
         del q, k, v, do, o, lse, devs
         torch.cuda.empty_cache()
+
+
+def copy_calibration(mib):
+    """One plain device copy of `mib` MiB (read and written once): a kernel of
+    known size against which HBM byte counters are scaled."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {mib} MiB read + {mib} MiB written")
+    del src, dst
 
 
 class ClockSampler:
@@ -609,10 +664,19 @@ def main():
                     help="comma-separated sequence lengths: print one JSON line per N "
                          "comparing with the three-kernel PyTorch path instead of the bench line")
     ap.add_argument("--sweep-d", type=int, default=64, choices=(64, 128),
-                    help="head dimension of the --sweep runs (B=1, H=16)")
+                    help="head dimension of the --sweep and --io runs (B=1, H=16)")
+    ap.add_argument("--io", default="",
+                    help="comma-separated sequence lengths: run the fused and the "
+                         "three-kernel forward twice each per N and nothing else, for "
+                         "counting HBM bytes under rocprofv3 --pmc")
     args = ap.parse_args()
     if args.sweep:
         run_sweep([int(x) for x in args.sweep.split(",")], D=args.sweep_d)
+        return
+    if args.io:
+        run_io([int(x) for x in args.io.split(",")], D=args.sweep_d)
+        if args.copy_mib > 0:
+            copy_calibration(args.copy_mib)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -676,15 +740,7 @@ def main():
         log(f"[bench] split forward: {split['ms']:.3f} ms")
 
     if args.copy_mib > 0:
-        import torch
-        n = args.copy_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] copy calibration: {args.copy_mib} MiB read + {args.copy_mib} MiB written")
-        del src, dst
+        copy_calibration(args.copy_mib)
 
     cpu = cpu_baseline(w, args.cpu_rows) if args.cpu_rows > 0 else None
 
