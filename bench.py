@@ -64,6 +64,7 @@ def kernel_algorithmic(w):
         "bwd_delta": ("hbm", 2.0 * w.B * w.H * w.N * w.D * el + 4.0 * w.B * w.H * w.N),
         "bwd_dkdv": ("mfma", 4 * unit),      # S, dP, dV, dK
         "bwd_dq": ("mfma", 1 * unit),        # dQ
+        "bwd_dkdv_dq": ("mfma", 5 * unit),   # both in one launch (small D = 64 grids)
         # merge of two partials: read O, O_part, LSE, LSE_part; write O, LSE
         "merge": ("hbm", 3.0 * w.B * w.H * w.N * (w.D * el + 4)),
     }
@@ -74,6 +75,7 @@ KERNEL_SOURCES = {
     "bwd_delta": ["fa_bwd.hip", "fa_device.h"],
     "bwd_dkdv": ["fa_bwd.hip", "fa_bwd_dkdv.h", "fa_bwd_d128.hip", "fa_device.h"],
     "bwd_dq": ["fa_bwd.hip", "fa_device.h"],
+    "bwd_dkdv_dq": ["fa_bwd.hip", "fa_bwd_dkdv.h", "fa_device.h"],
     "merge": ["fa_merge.hip", "fa_device.h"],
 }
 
@@ -712,7 +714,8 @@ def main():
         passes["fwd"] = {"ms": kernels["fwd"]["avg_ms"],
                          "tflops": f / (kernels["fwd"]["avg_ms"] / 1e3) / 1e12}
     if w.backward:
-        bms = sum(kernels[k]["avg_ms"] for k in ("bwd_delta", "bwd_dkdv", "bwd_dq") if k in kernels)
+        bms = sum(kernels[k]["avg_ms"] for k in ("bwd_delta", "bwd_dkdv", "bwd_dq", "bwd_dkdv_dq")
+                  if k in kernels)
         passes["bwd"] = {"ms": bms, "tflops": b / (bms / 1e3) / 1e12}
     for p in passes.values():
         p["pct_of_bf16_peak"] = 100.0 * p["tflops"] / PEAK_BF16_TFLOPS

@@ -80,7 +80,7 @@ int device_scratch(hipStream_t stream, void** out) {
 
 }  // namespace
 
-extern "C" int fa_version(void) { return 3; }
+extern "C" int fa_version(void) { return 4; }
 
 extern "C" const char* fa_status_string(int status) {
   switch (status) {
@@ -183,6 +183,11 @@ int launch_bwd(const fa::BwdArgs& a) {
     e = fa::launch_bwd_delta(a);
   }
   if (e != hipSuccess) return FA_ERR_HIP;
+  if (fa::bwd_combined(a)) {  // small D = 64 grids: dK/dV and dQ in one launch
+    fa::TimedLaunch t(FA_KERNEL_BWD_DKDV_DQ, a.stream);
+    e = fa::launch_bwd_dkdv_dq(a);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  }
   {
     fa::TimedLaunch t(FA_KERNEL_BWD_DKDV, a.stream);
     e = fa::launch_bwd_dkdv(a);

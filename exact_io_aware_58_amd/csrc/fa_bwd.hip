@@ -39,6 +39,12 @@
 //             may differ, so the seeds survive every tile).
 // The dq kernel recomputes S and dP a second time; that costs two extra
 // contractions per tile but removes every cross-workgroup reduction.
+// At D = 64 the two need the same registers and LDS, and on grids of at most
+// 8 workgroups per CU (e.g. B=8 H=12 N=1024, or one head group at N <= 8192)
+// they run as one launch (bwd_dkdv_dq_kernel): one kernel boundary fewer,
+// and dQ workgroups fill the CUs that the short causal dK/dV workgroups leave
+// idle (measured -5 to -24%; on larger grids the shared launch was 2-5%
+// slower, so those keep two launches).
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -98,13 +104,21 @@ struct DqTile<128> {
 
 constexpr int kDqBR = 128;  // query rows per workgroup (4 waves x 32)
 
+template <int D>
+constexpr int dq_stage_elems() { return 2 * DqTile<D>::BC * D; }
+
+// The dQ work of workgroup `pid` (see bwd_dq_kernel), on two LDS stages of
+// dq_stage_elems<D>() elements each.
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2)
-bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-              const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-              const float* __restrict__ nlse, const float* __restrict__ ndelta,
-              uint16_t* __restrict__ dQ, int N, float c, float scale, int nqt, int total,
-              int tile_major) {
+__device__ __forceinline__ void dq_body(const uint16_t* __restrict__ Q,
+                                        const uint16_t* __restrict__ K,
+                                        const uint16_t* __restrict__ V,
+                                        const uint16_t* __restrict__ dO,
+                                        const float* __restrict__ nlse,
+                                        const float* __restrict__ ndelta,
+                                        uint16_t* __restrict__ dQ, int N, float c, float scale,
+                                        int nqt, int total, int tile_major, int pid,
+                                        uint16_t* smem0, uint16_t* smem1) {
   constexpr int BC = DqTile<D>::BC;
   constexpr int TILE = BC * D;             // elements of one K or V tile
   constexpr int BLOCKS = TILE * 2 / 1024;  // 1 KiB blocks per tile
@@ -114,8 +128,6 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr int NKC = BC / 16;
   static_assert(BLOCKS == 8, "two blocks of K and two of V per wave");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t smem0[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t smem1[2 * TILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -123,7 +135,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int l32 = lane & 31, hh = lane >> 5;
 
   int bh, qt;
-  tile_of(blockIdx.x, total, nqt, tile_major, bh, qt);
+  tile_of(pid, total, nqt, tile_major, bh, qt);
   if (CAUSAL) qt = nqt - 1 - qt;  // longest rows first
   const int q0 = qt * kDqBR;
   const int wq0 = q0 + wave * 32;
@@ -292,6 +304,79 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         st_global8(dQr + db * 32 + 8 * g + 4 * hh, w);
       }
   }
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 2)
+bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+              const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+              const float* __restrict__ nlse, const float* __restrict__ ndelta,
+              uint16_t* __restrict__ dQ, int N, float c, float scale, int nqt, int total,
+              int tile_major) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem0[dq_stage_elems<D>()];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem1[dq_stage_elems<D>()];
+  dq_body<T, D, CAUSAL>(Q, K, V, dO, nlse, ndelta, dQ, N, c, scale, nqt, total, tile_major,
+                        blockIdx.x, smem0, smem1);
+}
+
+// D = 64: the dK/dV and dQ workgroups of one backward in a single launch.
+// Both need the same registers and LDS and neither reads the other's output,
+// so sharing a grid removes a kernel boundary and lets one kernel's short
+// tail tiles fill in beside the other's.  Roles alternate every 8 workgroups
+// (one per XCD), so each XCD gets the same mix and, within a role, workgroup
+// `pid` keeps pid % 8 == its XCD as the tile order assumes.
+template <typename T, bool CAUSAL>
+__global__ void __launch_bounds__(256, 2)
+bwd_dkdv_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                   const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                   const float* __restrict__ nlse, const float* __restrict__ ndelta,
+                   uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK,
+                   uint16_t* __restrict__ dV, int N, float c, float scale, int nkt, int total_kv,
+                   int tm_kv, int nqt, int total_q, int tm_q) {
+  constexpr int D = 64;
+  constexpr int E = dkv_stage_elems<D>() > dq_stage_elems<D>() ? dkv_stage_elems<D>()
+                                                               : dq_stage_elems<D>();
+  __shared__ __attribute__((aligned(1024))) uint16_t smem0[E];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem1[E];
+  const int b = blockIdx.x;
+  const int pid = ((b >> 4) << 3) | (b & 7);
+  if (((b >> 3) & 1) == 0) {
+    if (pid < total_kv)
+      dkdv_body<T, D, CAUSAL>(Q, K, V, dO, nlse, ndelta, dK, dV, N, c, scale, nkt, total_kv,
+                              tm_kv, pid, smem0, smem1);
+  } else {
+    if (pid < total_q)
+      dq_body<T, D, CAUSAL>(Q, K, V, dO, nlse, ndelta, dQ, N, c, scale, nqt, total_q, tm_q, pid,
+                            smem0, smem1);
+  }
+}
+
+template <typename T, bool CAUSAL>
+static hipError_t dkdv_dq64(const BwdArgs& a) {
+  const int nkt = (a.N + kDkvKeys - 1) / kDkvKeys;
+  const int total_kv = nkt * a.B * a.H;
+  const int nqt = (a.N + kDqBR - 1) / kDqBR;
+  const int total_q = nqt * a.B * a.H;
+  const int mx = total_kv > total_q ? total_kv : total_q;
+  const unsigned grid = 16u * (unsigned)((mx + 7) / 8);
+  hipLaunchKernelGGL((bwd_dkdv_dq_kernel<T, CAUSAL>), dim3(grid), dim3(256), 0, a.stream,
+                     (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
+                     (const uint16_t*)a.dO, a.nlse, a.ndelta, (uint16_t*)a.dQ, (uint16_t*)a.dK,
+                     (uint16_t*)a.dV, a.N, a.scale * kLog2e, a.scale, nkt, total_kv,
+                     tile_major(CAUSAL, nkt, total_kv), nqt, total_q,
+                     tile_major(CAUSAL, nqt, total_q));
+  return hipGetLastError();
+}
+
+bool bwd_combined(const BwdArgs& a) {
+  if (a.D != 64) return false;
+  const long n = (long)((a.N + kDqBR - 1) / kDqBR) * a.B * a.H;
+  return 2 * n <= 8L * cu_count();  // grids of at most a few rounds
+}
+
+hipError_t launch_bwd_dkdv_dq(const BwdArgs& a) {
+  if (a.dtype == kBF16) return a.causal ? dkdv_dq64<BF16, true>(a) : dkdv_dq64<BF16, false>(a);
+  return a.causal ? dkdv_dq64<F16, true>(a) : dkdv_dq64<F16, false>(a);
 }
 
 // ------------------------------------------------------------------ launchers

@@ -29,13 +29,23 @@ struct DkvTile<128> {
 
 constexpr int kDkvKeys = 128;  // key rows per workgroup (4 waves x 32)
 
+// LDS elements of one dK/dV stage: Q, dO, then 64 -LSE/scale + 64 -Delta floats.
+template <int D>
+constexpr int dkv_stage_elems() { return 2 * DkvTile<D>::BR * D + 2 * 64 * 2; }
+
+// The dK/dV work of workgroup `pid` (see bwd_dkdv_kernel), on two LDS
+// stages of dkv_stage_elems<D>() elements each.
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, DkvTile<D>::MIN_WG)
-bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                const float* __restrict__ nlse, const float* __restrict__ ndelta,
-                uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, float c,
-                float scale, int nkt, int total, int tile_major) {
+__device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ Q,
+                                          const uint16_t* __restrict__ K,
+                                          const uint16_t* __restrict__ V,
+                                          const uint16_t* __restrict__ dO,
+                                          const float* __restrict__ nlse,
+                                          const float* __restrict__ ndelta,
+                                          uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+                                          int N, float c, float scale, int nkt, int total,
+                                          int tile_major, int pid, uint16_t* smem0,
+                                          uint16_t* smem1) {
   constexpr int BR = DkvTile<D>::BR;
   constexpr int TILE = BR * D;                  // elements of one Q or dO tile
   constexpr int BLOCKS = TILE * 2 / 1024;       // 1 KiB blocks per tile
@@ -44,10 +54,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr int NDB = D / 32;
   static_assert(BLOCKS == 8, "two blocks of Q and two of dO per wave");
 
-  // Two stages in separate arrays, the loop unrolled by two: loads into one
-  // stage provably never alias reads of the other (no spurious waits).
-  __shared__ __attribute__((aligned(1024))) uint16_t smem0[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint16_t smem1[STAGE];
+  static_assert(STAGE == dkv_stage_elems<D>(), "stage layout");
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -55,7 +62,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int l32 = lane & 31, hh = lane >> 5;
 
   int bh, kt;  // causal: small kt has the most queries, runs first
-  tile_of(blockIdx.x, total, nkt, tile_major, bh, kt);
+  tile_of(pid, total, nkt, tile_major, bh, kt);
   const int k0 = kt * kDkvKeys;
   const int wk0 = k0 + wave_u * 32;
   const int mykey = wk0 + l32;
@@ -268,6 +275,21 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         st_global8(dVr + d, wv);
       }
   }
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, DkvTile<D>::MIN_WG)
+bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                const float* __restrict__ nlse, const float* __restrict__ ndelta,
+                uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, float c,
+                float scale, int nkt, int total, int tile_major) {
+  // Two stages in separate arrays, the loop unrolled by two: loads into one
+  // stage provably never alias reads of the other (no spurious waits).
+  __shared__ __attribute__((aligned(1024))) uint16_t smem0[dkv_stage_elems<D>()];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem1[dkv_stage_elems<D>()];
+  dkdv_body<T, D, CAUSAL>(Q, K, V, dO, nlse, ndelta, dK, dV, N, c, scale, nkt, total,
+                          tile_major, blockIdx.x, smem0, smem1);
 }
 
 // Launches the dK/dV kernel for one element type, head dimension and mask.

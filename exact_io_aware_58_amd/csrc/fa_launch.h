@@ -79,6 +79,9 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);
 // dK/dV at D = 128 without a mask (fa_bwd_d128.hip, its own compile flags).
 hipError_t launch_bwd_dkdv_d128_nomask(const BwdArgs& a);
+// D = 64 grids of a few rounds: dK/dV and dQ in one launch (fa_bwd.hip).
+bool bwd_combined(const BwdArgs& a);
+hipError_t launch_bwd_dkdv_dq(const BwdArgs& a);
 
 // Optional per-kernel event timing (fa_timing.cpp).  No-ops when disabled.
 struct TimedLaunch {

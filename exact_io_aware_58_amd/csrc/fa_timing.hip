@@ -124,6 +124,7 @@ extern "C" const char* fa_kernel_name(int kernel_id) {
     case FA_KERNEL_BWD_DKDV: return "bwd_dkdv";
     case FA_KERNEL_BWD_DQ: return "bwd_dq";
     case FA_KERNEL_MERGE: return "merge";
+    case FA_KERNEL_BWD_DKDV_DQ: return "bwd_dkdv_dq";
     default: return "unknown";
   }
 }

@@ -19,7 +19,8 @@ FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
 FA_KERNEL_FWD, FA_KERNEL_BWD_DELTA, FA_KERNEL_BWD_DKDV, FA_KERNEL_BWD_DQ = 0, 1, 2, 3
 FA_KERNEL_MERGE = 4
-FA_KERNEL_COUNT = 5
+FA_KERNEL_BWD_DKDV_DQ = 5
+FA_KERNEL_COUNT = 6
 
 # Every symbol include/fa.h declares, with (restype, argtypes).
 _c_int, _c_size, _vp, _f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float

@@ -211,7 +211,10 @@ enum {
   FA_KERNEL_BWD_DKDV = 2,     /* backward: dK, dV                        */
   FA_KERNEL_BWD_DQ = 3,       /* backward: dQ                            */
   FA_KERNEL_MERGE = 4,        /* fa_merge                                */
-  FA_KERNEL_COUNT = 5
+  FA_KERNEL_BWD_DKDV_DQ = 5,  /* backward: dK, dV and dQ in one launch,
+                                 used instead of the two above for D = 64
+                                 grids of at most 8 workgroups per CU     */
+  FA_KERNEL_COUNT = 6
 };
 int fa_timing_enable(int on);
 int fa_timing_read(int kernel_id, long long* launches, double* total_ms, long long* dropped);

@@ -50,7 +50,7 @@ P = [A + 0x1000 * i for i in range(12)]
 
 
 def test_version_and_status_strings(fa):
-    assert fa.fa_version() >= 2
+    assert fa.fa_version() >= 4
     for code in (0, -1, -2, -3, -4):
         assert fa.fa_status_string(code) != "unknown status"
     assert fa.fa_status_string(99) == "unknown status"
@@ -127,8 +127,8 @@ def test_timing_read_bounds(fa):
         fa.fa_timing_read(fa.FA_KERNEL_COUNT)
     n, ms, dropped = fa.fa_timing_read(fa.FA_KERNEL_FWD)
     assert n == 0 and ms == 0.0 and dropped == 0
-    assert [fa.fa_kernel_name(i) for i in range(5)] == ["fwd", "bwd_delta", "bwd_dkdv", "bwd_dq",
-                                                        "merge"]
+    assert [fa.fa_kernel_name(i) for i in range(fa.FA_KERNEL_COUNT)] == [
+        "fwd", "bwd_delta", "bwd_dkdv", "bwd_dq", "merge", "bwd_dkdv_dq"]
     assert fa.fa_kernel_name(fa.FA_KERNEL_COUNT) == "unknown"
 
 

@@ -31,6 +31,7 @@ def test_kernel_work_per_launch():
     assert alg["fwd"] == ("mfma", 2 * unit)
     assert alg["bwd_dkdv"] == ("mfma", 4 * unit)
     assert alg["bwd_dq"] == ("mfma", 1 * unit)
+    assert alg["bwd_dkdv_dq"] == ("mfma", 5 * unit)
     rows = w.B * w.H * w.N
     assert alg["bwd_delta"] == ("hbm", 2.0 * rows * w.D * 2 + 4.0 * rows)
     assert alg["merge"] == ("hbm", 3.0 * rows * (w.D * 2 + 4))
