@@ -149,6 +149,51 @@ def test_joint_key_value_permutation_long_forward():
     assert eo <= 2e-2 and er <= 2e-2 and el <= 1e-4
 
 
+@pytest.mark.parametrize("wname", ["c4", "c5"])
+def test_key_shift_long_forward(wname):
+    """Adding one vector c to every key changes every visible score of row i
+    by the same scale * q_i . c: O is unchanged and LSE_i moves by exactly
+    that amount.  Grid-valued Q, K, V (inputs.draw_grid: multiples of 1/16)
+    and c in {+1/4, -1/4}^D keep K + c exact in bf16, so the shifted run sees
+    exactly the shifted inputs; every row is checked (c4 no mask, c5 causal)."""
+    w = inputs.WORKLOADS[wname]
+    say(f"[key shift {w.name}] all rows")
+    qx, q = _grid(w, "q")
+    _, k = _grid(w, "k")
+    _, v = _grid(w, "v")
+    sign = np.random.default_rng(w.seed + 4000).integers(0, 2, w.D) * 2 - 1
+    cvec = 0.25 * sign.astype(np.float64)
+    kc = (k.float() + torch.from_numpy(cvec).float().cuda()).to(torch.bfloat16)
+    o, lse = fa.forward(q, k, v, w.scale, w.causal)
+    o2, lse2 = fa.forward(q, kc, v, w.scale, w.causal)
+    torch.cuda.synchronize()
+    a, b = to_f64(o), to_f64(o2)
+    eo, er = max_abs(a, b), rel_to_max(b, a)
+    shift = w.scale * (qx.astype(np.float64) @ cvec)
+    el = max_abs(to_f64(lse2) - to_f64(lse), shift)
+    say(f"    O max abs {eo:.2e} (rel-to-max {er:.2e}); LSE shift max abs err {el:.2e}")
+    assert eo <= 2e-2 and er <= 2e-2 and el <= 1e-3
+
+
+def test_query_permutation_long_forward():
+    """Unmasked N = 16384, D = 128: permuting the queries permutes the rows
+    of O and LSE (each row is computed from its own query alone)."""
+    w = inputs.WORKLOADS["c4"]
+    say(f"[query permutation {w.name}] all rows")
+    _, q = _draw(w, "q")
+    _, k = _draw(w, "k")
+    _, v = _draw(w, "v")
+    o, lse = fa.forward(q, k, v, w.scale, False)
+    perm = torch.from_numpy(np.random.default_rng(w.seed + 5000).permutation(w.N)).cuda()
+    o2, lse2 = fa.forward(q[:, :, perm].contiguous(), k, v, w.scale, False)
+    torch.cuda.synchronize()
+    a, b = to_f64(o[:, :, perm]), to_f64(o2)
+    eo, er = max_abs(a, b), rel_to_max(b, a)
+    el = max_abs(to_f64(lse[:, :, perm]), to_f64(lse2))
+    say(f"    O max abs {eo:.2e} (rel-to-max {er:.2e}); LSE max abs {el:.2e}")
+    assert eo <= 2e-2 and er <= 2e-2 and el <= 1e-4
+
+
 def test_zero_queries_d128_training():
     """Q = 0 at the D = 128 training shape (B=1, H=16, N=16384, no mask):
     every row of O is the mean of V, dK = 0 exactly, and dQ, dV match their
