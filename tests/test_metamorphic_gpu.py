@@ -150,12 +150,16 @@ def test_joint_key_value_permutation_long_forward():
 
 
 @pytest.mark.parametrize("wname", ["c4", "c5"])
-def test_key_shift_long_forward(wname):
+def test_key_shift_long(wname):
     """Adding one vector c to every key changes every visible score of row i
     by the same scale * q_i . c: O is unchanged and LSE_i moves by exactly
-    that amount.  Grid-valued Q, K, V (inputs.draw_grid: multiples of 1/16)
-    and c in {+1/4, -1/4}^D keep K + c exact in bf16, so the shifted run sees
-    exactly the shifted inputs; every row is checked (c4 no mask, c5 causal)."""
+    that amount.  P is then unchanged, so are dV = P^T dO and dS, and since
+    every row of dS sums to zero (sum_j P_ij (dP_ij - Delta_i) = 0) dQ =
+    scale dS (K + c) and dK = scale dS^T Q are unchanged too: at c5 the
+    backward is checked as well.  Grid-valued Q, K, V, dO (inputs.draw_grid:
+    multiples of 1/16) and c in {+1/4, -1/4}^D keep K + c exact in bf16, so
+    the shifted run sees exactly the shifted inputs; every row is checked
+    (c4 no mask, c5 causal)."""
     w = inputs.WORKLOADS[wname]
     say(f"[key shift {w.name}] all rows")
     qx, q = _grid(w, "q")
@@ -173,6 +177,14 @@ def test_key_shift_long_forward(wname):
     el = max_abs(to_f64(lse2) - to_f64(lse), shift)
     say(f"    O max abs {eo:.2e} (rel-to-max {er:.2e}); LSE shift max abs err {el:.2e}")
     assert eo <= 2e-2 and er <= 2e-2 and el <= 1e-3
+    if w.backward:
+        _, do = _grid(w, "do")
+        g1 = fa.backward(q, k, v, o, do, lse, w.scale, w.causal)
+        g2 = fa.backward(q, kc, v, o2, do, lse2, w.scale, w.causal)
+        torch.cuda.synchronize()
+        errs = [rel_to_max(to_f64(b2), to_f64(b1)) for b1, b2 in zip(g1, g2)]
+        say("    rel-to-max dQ={:.2e} dK={:.2e} dV={:.2e}".format(*errs))
+        assert max(errs) <= 5e-2
 
 
 def test_query_permutation_long_forward():
