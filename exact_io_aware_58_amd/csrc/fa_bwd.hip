@@ -107,8 +107,9 @@ constexpr int kDqBR = 128;  // query rows per workgroup (4 waves x 32)
 template <int D>
 constexpr int dq_stage_elems() { return 2 * DqTile<D>::BC * D; }
 
-// The dQ work of workgroup `pid` (see bwd_dq_kernel), on two LDS stages of
-// dq_stage_elems<D>() elements each.
+// The dQ work of workgroup `pid` (the query-resident kernel described at
+// the top of this file), on two LDS stages of dq_stage_elems<D>() elements
+// each.  Shared by bwd_dq_kernel and the combined launch below.
 template <typename T, int D, bool CAUSAL>
 __device__ __forceinline__ void dq_body(const uint16_t* __restrict__ Q,
                                         const uint16_t* __restrict__ K,

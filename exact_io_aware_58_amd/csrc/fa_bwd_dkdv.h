@@ -33,8 +33,10 @@ constexpr int kDkvKeys = 128;  // key rows per workgroup (4 waves x 32)
 template <int D>
 constexpr int dkv_stage_elems() { return 2 * DkvTile<D>::BR * D + 2 * 64 * 2; }
 
-// The dK/dV work of workgroup `pid` (see bwd_dkdv_kernel), on two LDS
-// stages of dkv_stage_elems<D>() elements each.
+// The dK/dV work of workgroup `pid` (the key-resident kernel described at
+// the top of fa_bwd.hip), on two LDS stages of dkv_stage_elems<D>()
+// elements each.  Shared by bwd_dkdv_kernel and, at D = 64, the combined
+// dK/dV + dQ launch (fa_bwd.hip).
 template <typename T, int D, bool CAUSAL>
 __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ Q,
                                           const uint16_t* __restrict__ K,
@@ -49,12 +51,9 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ Q,
   constexpr int BR = DkvTile<D>::BR;
   constexpr int TILE = BR * D;                  // elements of one Q or dO tile
   constexpr int BLOCKS = TILE * 2 / 1024;       // 1 KiB blocks per tile
-  constexpr int STAGE = 2 * TILE + 2 * 64 * 2;  // Q, dO, then 64 -LSE/scale + 64 -Delta floats
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
   static_assert(BLOCKS == 8, "two blocks of Q and two of dO per wave");
-
-  static_assert(STAGE == dkv_stage_elems<D>(), "stage layout");
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
