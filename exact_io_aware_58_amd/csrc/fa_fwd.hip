@@ -136,6 +136,21 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[NKB], u32x4 (&pk)
   lpart += rs;
 }
 
+// keep_if_le reads MFMA results from inside inline asm, where the compiler
+// does not count the wait states a vector read of an MFMA destination needs.
+// This block supplies them once per masked tile: 24 wait states (three
+// s_nop 7), more than a 32x32 MFMA's result needs, and it takes the scores
+// as operands so nothing that produces them can move past it.
+template <int NKB>
+__device__ __forceinline__ void mfma_result_guard(f32x16 (&s)[NKB]) {
+  static_assert(NKB == 2 || NKB == 4, "score blocks per tile");
+  if constexpr (NKB == 2)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]));
+  else
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]), "+v"(s[3]));
+}
+
 // Sets the scores of invisible keys to -inf.  Register r of block kb holds
 // key ts + 4hh + 32kb + 8(r/4) + r%4; keys at or past Nk, and (causal) past
 // `last` (the lane's last visible key), are dropped.  The first form keeps
@@ -146,6 +161,7 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[NKB], u32x4 (&pk)
 template <bool CAUSAL, int NKB>
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[NKB], int ts, int Nk, int last, int hh) {
   if constexpr (CAUSAL || NKB == 4) {
+    mfma_result_guard(s);
     const int lim = (CAUSAL ? min(Nk - 1, last) : Nk - 1) - ts - 4 * hh;
     const float ninf = -INFINITY;
 #pragma unroll
