@@ -195,10 +195,12 @@ __device__ inline i32x4 rsrc_words(const void* base, uint32_t bytes) {
 // flight.  The kernels order them explicitly (vmcnt waits before the
 // barriers that publish a buffer); the "memory" clobber keeps other memory
 // accesses from moving across.  M0 is only used this way in these kernels.
+// An LDS-direct load reading M0 needs one wait state after the scalar write
+// of M0 (the s_nop 0); the compiler cannot insert it inside the asm.
 __device__ inline void lds_dma16(const i32x4& r, const uint16_t* lds_block, uint32_t goff) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(
       (__attribute__((address_space(3))) const uint16_t*)lds_block);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(goff), "s"(r)
                : "memory");
@@ -207,7 +209,7 @@ __device__ inline void lds_dma16(const i32x4& r, const uint16_t* lds_block, uint
 __device__ inline void lds_dma4(const i32x4& r, const void* lds_block, uint32_t goff) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(
       (__attribute__((address_space(3))) const char*)lds_block);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :
                : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(goff), "s"(r)
                : "memory");
