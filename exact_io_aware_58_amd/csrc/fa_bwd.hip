@@ -164,7 +164,7 @@ __device__ __forceinline__ void dq_body(const uint16_t* __restrict__ Q,
 
   const int nfull = min(N / BC, CAUSAL ? (q0 + 1) / BC : ntiles);
   // The first key tile travels while Q and dO load.
-  if (nfull > 0) dma(smem0, 0);
+  if (ntiles > 0) dma(smem0, 0);
 
   u32x4 qf[NDC], gf[NDC];
 #pragma unroll
@@ -266,13 +266,14 @@ __device__ __forceinline__ void dq_body(const uint16_t* __restrict__ Q,
   };
 
   // Tiles wholly visible to every row of the workgroup (no tail, not past
-  // the causal diagonal) run the straight-line body, double-buffered; the
-  // remaining ones (at the end) the masked body, unpipelined.
+  // the causal diagonal) come first and run the straight-line body; the rest
+  // (at the end) run the masked body.  All of them are double-buffered: tile
+  // t sits in stage t % 2 and the next one loads while it is consumed.
   int t = 0;
   wait_dma();
   __syncthreads();
   for (; t < nfull; t += 2) {
-    if (t + 1 < nfull) dma(smem1, (t + 1) * BC);
+    if (t + 1 < ntiles) dma(smem1, (t + 1) * BC);
     tile(smem0, t * BC, std::false_type());
     wait_dma();
     __syncthreads();
@@ -280,16 +281,22 @@ __device__ __forceinline__ void dq_body(const uint16_t* __restrict__ Q,
       t += 1;
       break;
     }
-    if (t + 2 < nfull) dma(smem0, (t + 2) * BC);
+    if (t + 2 < ntiles) dma(smem0, (t + 2) * BC);
     tile(smem1, (t + 1) * BC, std::false_type());
     wait_dma();
     __syncthreads();
   }
+  // Each branch names its stages directly, so the compiler can tell the
+  // loads into one stage from the reads of the other.
   for (; t < ntiles; ++t) {
-    dma(smem0, t * BC);
+    if (t & 1) {
+      if (t + 1 < ntiles) dma(smem0, (t + 1) * BC);
+      tile(smem1, t * BC, std::true_type());
+    } else {
+      if (t + 1 < ntiles) dma(smem1, (t + 1) * BC);
+      tile(smem0, t * BC, std::true_type());
+    }
     wait_dma();
-    __syncthreads();
-    tile(smem0, t * BC, std::true_type());
     __syncthreads();
   }
 

@@ -216,20 +216,29 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ Q,
       }
   };
   // Causal: the first tiles (queries k0 .. k0+127) straddle the diagonal of
-  // this workgroup's keys and take the masked body, unpipelined; every later
-  // tile is wholly visible and runs the straight-line body, double-buffered.
+  // this workgroup's keys and take the masked body; every later tile is
+  // wholly visible and runs the straight-line body.  All of them are
+  // double-buffered, tile t in stage t % 2 (the diagonal spans an even
+  // number of tiles, so the straight-line loop starts in stage 0).
   int t = 0;
+  static_assert((kDkvKeys / BR) % 2 == 0, "the diagonal spans an even number of tiles");
   const int ndiag = CAUSAL ? min(ntiles, kDkvKeys / BR) : 0;
-  for (; t < ndiag; ++t) {
-    if (t > 0) dma(smem0, qstart + t * BR);
-    wait_dma();
-    __syncthreads();
-    tile(smem0, qstart + t * BR, std::true_type());
-    __syncthreads();
-  }
-  if (t > 0 && t < ntiles) dma(smem0, qstart + t * BR);
   wait_dma();
   __syncthreads();
+  for (; t < ndiag; t += 2) {
+    if (t + 1 < ntiles) dma(smem1, qstart + (t + 1) * BR);
+    tile(smem0, qstart + t * BR, std::true_type());
+    wait_dma();
+    __syncthreads();
+    if (t + 1 >= ndiag) {
+      t += 1;
+      break;
+    }
+    if (t + 2 < ntiles) dma(smem0, qstart + (t + 2) * BR);
+    tile(smem1, qstart + (t + 1) * BR, std::true_type());
+    wait_dma();
+    __syncthreads();
+  }
   if constexpr (D == 128 && !CAUSAL) {
     // One tile per iteration, the stage picked by parity.  With the MFMA
     // results kept in VGPRs (that instantiation is built in its own unit,

@@ -316,16 +316,21 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   };
 
-  // Tiles visible to every row (no tail, not past the causal diagonal):
-  // straight-line body, double-buffered; the rest (at the end): masked body.
+  // Tiles visible to every row (no tail, not past the causal diagonal) come
+  // first: straight-line body, double-buffered.  The rest (the causal
+  // diagonal, a ragged tail) take the masked body.  The first of those is
+  // prefetched like a full tile (during the last full one, or by the
+  // prologue when there is none) and lands in stage nfull % 2; any further
+  // one loads on its own (a loop that prefetched every masked tile measured
+  // slower on short causal sequences).
   const int nfull = min(Nk / BC, CAUSAL ? max(0, q0 + dlt + 1) / BC : ntiles);
   int t = 0;
-  if (nfull > 0) dma(smem0, 0);
+  if (ntiles > 0) dma(smem0, 0);
   wait_dma();
   __syncthreads();
   for (; t < nfull; t += 2) {
     // even tile in stage 0 while the odd one lands in stage 1, then swap
-    if (t + 1 < nfull) dma(smem1, (t + 1) * BC);
+    if (t + 1 < ntiles) dma(smem1, (t + 1) * BC);
     tile(smem0, t * BC, std::false_type());
     wait_dma();
     __syncthreads();
@@ -333,10 +338,18 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       t += 1;
       break;
     }
-    if (t + 2 < nfull) dma(smem0, (t + 2) * BC);
+    if (t + 2 < ntiles) dma(smem0, (t + 2) * BC);
     tile(smem1, (t + 1) * BC, std::false_type());
     wait_dma();
     __syncthreads();
+  }
+  if (t < ntiles) {
+    if (t & 1)
+      tile(smem1, t * BC, std::true_type());
+    else
+      tile(smem0, t * BC, std::true_type());
+    __syncthreads();
+    ++t;
   }
   for (; t < ntiles; ++t) {
     dma(smem0, t * BC);
