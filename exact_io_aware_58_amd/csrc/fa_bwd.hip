@@ -286,16 +286,12 @@ __device__ __forceinline__ void dq_body(const uint16_t* __restrict__ Q,
     wait_dma();
     __syncthreads();
   }
-  // Each branch names its stages directly, so the compiler can tell the
-  // loads into one stage from the reads of the other.
+  // One copy of the masked body, its stage picked at run time (a copy per
+  // stage made the compiler spill registers at D = 128).
   for (; t < ntiles; ++t) {
-    if (t & 1) {
-      if (t + 1 < ntiles) dma(smem0, (t + 1) * BC);
-      tile(smem1, t * BC, std::true_type());
-    } else {
-      if (t + 1 < ntiles) dma(smem1, (t + 1) * BC);
-      tile(smem0, t * BC, std::true_type());
-    }
+    const bool odd = t & 1;
+    if (t + 1 < ntiles) dma(odd ? smem0 : smem1, (t + 1) * BC);
+    tile(odd ? smem1 : smem0, t * BC, std::true_type());
     wait_dma();
     __syncthreads();
   }

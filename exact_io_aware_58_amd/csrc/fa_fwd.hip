@@ -344,10 +344,9 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     __syncthreads();
   }
   if (t < ntiles) {
-    if (t & 1)
-      tile(smem1, t * BC, std::true_type());
-    else
-      tile(smem0, t * BC, std::true_type());
+    // one copy of the masked body (a second one, per stage, made the
+    // compiler spill registers at D = 128); no load is in flight here
+    tile((t & 1) ? smem1 : smem0, t * BC, std::true_type());
     __syncthreads();
     ++t;
   }
