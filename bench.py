@@ -550,6 +550,51 @@ def run_sweep(ns, heads=16, D=64, reps=5):
         torch.cuda.empty_cache()
 
 
+def run_update_probe(mib=256, passes=8, reps=3):
+    """Rate of fp32 updates to device memory (plain store, plain
+    read-modify-write, fp32 atomic add), from the probe library built beside
+    libfa.so: each pass updates every float of a `mib` MiB buffer once, one
+    lane per element, 256 contiguous bytes per wave.  The atomic adds are
+    checked (every element ends at passes x launches).  Prints one JSON line:
+    the best of `reps` timed launches per mode, as GB/s of 4-byte updates."""
+    import ctypes
+
+    import torch
+    from exact_io_aware_58_amd import build
+
+    if not os.path.exists(build.PROBE_LIB):
+        raise RuntimeError(f"{build.PROBE_LIB} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(build.PROBE_LIB)
+    lib.fa_probe_update.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                    ctypes.c_void_p]
+    lib.fa_probe_update.restype = ctypes.c_int
+    n = mib * (1 << 20) // 4
+    buf = torch.zeros(n, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    row = {"probe": "fp32 updates", "buffer_mib": mib, "passes_per_launch": passes,
+           "unit": "GB/s of 4-byte updates"}
+    for mode, name in ((0, "store"), (1, "read_modify_write"), (2, "atomic_add")):
+        buf.zero_()
+        launches = 0
+        best = None
+        for r in range(reps + 1):  # the first launch is a warm-up
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = lib.fa_probe_update(mode, buf.data_ptr(), n, passes, stream.cuda_stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"fa_probe_update({mode}) returned {rc}")
+            launches += 1
+            if r > 0:
+                ms = e0.elapsed_time(e1)
+                best = ms if best is None else min(best, ms)
+        row[name] = n * 4 * passes / (best / 1e3) / 1e9
+        if mode == 2:
+            row["atomic_add_checked"] = bool((buf == float(passes * launches)).all().item())
+    print(json.dumps(row), flush=True)
+
+
 def copy_calibration(mib):
     """One plain device copy of `mib` MiB (read and written once): a kernel of
     known size against which HBM byte counters are scaled."""
@@ -671,7 +716,13 @@ def main():
                     help="comma-separated sequence lengths: run the fused and the "
                          "three-kernel forward twice each per N and nothing else, for "
                          "counting HBM bytes under rocprofv3 --pmc")
+    ap.add_argument("--probe", action="store_true",
+                    help="rate of fp32 stores, read-modify-writes and atomic adds to "
+                         "device memory (the probe library), then exit")
     args = ap.parse_args()
+    if args.probe:
+        run_update_probe()
+        return
     if args.sweep:
         run_sweep([int(x) for x in args.sweep.split(",")], D=args.sweep_d)
         return

@@ -19,6 +19,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+# Measurement probe, a library of its own (not part of the attention ABI).
+PROBE_SOURCE = "fa_probe.hip"
+PROBE_LIB = os.path.join(PKG, "libfa_probe.so")
 REPORT = os.path.join(BUILD, "resource_usage.json")
 SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_d128.hip", "fa_merge.hip",
            "fa_timing.hip"]
@@ -98,6 +101,9 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    _run([cc, *compile_flags(), "-shared", "-o", tmp, os.path.join(CSRC, PROBE_SOURCE)], verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

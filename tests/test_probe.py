@@ -1,0 +1,54 @@
+"""The update-rate probe library (measurement support beside libfa.so): it
+exports its entry point, rejects bad arguments before any HIP call, and on
+the GPU its atomic and read-modify-write passes add exactly once per
+element per pass."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from exact_io_aware_58_amd import build
+
+pytestmark = pytest.mark.skipif(not os.path.exists(build.PROBE_LIB),
+                                reason="libfa_probe.so not built")
+
+HIP_ERROR_INVALID_VALUE = 1
+
+
+def _lib():
+    lib = ctypes.CDLL(build.PROBE_LIB)
+    lib.fa_probe_update.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                    ctypes.c_void_p]
+    lib.fa_probe_update.restype = ctypes.c_int
+    return lib
+
+
+def test_probe_exports_its_entry_point():
+    out = subprocess.run(["nm", "-D", "--defined-only", build.PROBE_LIB], capture_output=True,
+                         text=True, check=True).stdout
+    assert "fa_probe_update" in {line.split()[-1] for line in out.splitlines() if line.strip()}
+
+
+@pytest.mark.parametrize("mode,buf,n,passes", [(3, 256, 64, 1), (-1, 256, 64, 1),
+                                               (0, None, 64, 1), (1, 256, 0, 1),
+                                               (2, 256, 64, 0)])
+def test_probe_rejects_bad_arguments(mode, buf, n, passes):
+    # returns before any HIP call, so no GPU is needed
+    assert _lib().fa_probe_update(mode, buf, n, passes, None) == HIP_ERROR_INVALID_VALUE
+
+
+@pytest.mark.gpu
+def test_probe_updates_every_element_once_per_pass():
+    torch = pytest.importorskip("torch")
+    lib = _lib()
+    n = (1 << 18) + 77  # a ragged tail past the last full wave
+    buf = torch.zeros(n, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    assert lib.fa_probe_update(2, buf.data_ptr(), n, 3, s) == 0
+    assert lib.fa_probe_update(1, buf.data_ptr(), n, 2, s) == 0
+    torch.cuda.synchronize()
+    assert bool((buf == 5.0).all().item())
+    assert lib.fa_probe_update(0, buf.data_ptr(), n, 1, s) == 0
+    torch.cuda.synchronize()
+    assert bool((buf == 1.0).all().item())
