@@ -550,13 +550,15 @@ def run_sweep(ns, heads=16, D=64, reps=5):
         torch.cuda.empty_cache()
 
 
-def run_update_probe(mib=256, passes=8, reps=3):
+def run_update_probe(mib=256, passes=8, reps=3, mfma_s=2.5):
     """Rate of fp32 updates to device memory (plain store, plain
     read-modify-write, fp32 atomic add), from the probe library built beside
     libfa.so: each pass updates every float of a `mib` MiB buffer once, one
     lane per element, 256 contiguous bytes per wave.  The atomic adds are
     checked (every element ends at passes x launches).  Prints one JSON line:
-    the best of `reps` timed launches per mode, as GB/s of 4-byte updates."""
+    the best of `reps` timed launches per mode, as GB/s of 4-byte updates.
+    Then the register-only bf16 MFMA rate over `mfma_s` seconds of launches,
+    with the shader clock sampled meanwhile (a second JSON line)."""
     import ctypes
 
     import torch
@@ -593,6 +595,53 @@ def run_update_probe(mib=256, passes=8, reps=3):
         if mode == 2:
             row["atomic_add_checked"] = bool((buf == float(passes * launches)).all().item())
     print(json.dumps(row), flush=True)
+    del buf
+
+    # Register-only bf16 MFMA loop: 8 four-wave workgroups per CU, launches
+    # back to back for `mfma_s` seconds with the shader clock sampled.
+    lib.fa_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_probe_mfma.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = cus * 8, 2000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    flops = blocks * 4 * iters * 4 * 2.0 * 32 * 32 * 16
+
+    def launch():
+        rc = lib.fa_probe_mfma(out.data_ptr(), blocks, iters, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"fa_probe_mfma returned {rc}")
+
+    launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(20):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per = e0.elapsed_time(e1) / 20
+    count = max(20, int(mfma_s * 1e3 / per))
+    clock = ClockSampler()
+    t0 = time.perf_counter()
+    clock.start()
+    e0.record(stream)
+    for _ in range(count):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    clock.stop()
+    window = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / count
+    tflops = flops / (ms / 1e3) / 1e12
+    mfma = {"probe": "register-only bf16 MFMA (32x32x16, 4 independent chains per wave)",
+            "workgroups": blocks, "waves_per_cu": 32, "launches": count, "ms_per_launch": ms,
+            "tflops": tflops, "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+            "sclk": clock.summary(window)}
+    if mfma["sclk"]:
+        peak_clk = PEAK_BF16_TFLOPS * mfma["sclk"]["mean_mhz"] / NOMINAL_SCLK_MHZ
+        mfma["peak_at_measured_clock"] = peak_clk
+        mfma["pct_of_peak_at_measured_clock"] = 100.0 * tflops / peak_clk
+    print(json.dumps(mfma), flush=True)
 
 
 def copy_calibration(mib):
