@@ -15,6 +15,8 @@
 
 #include <stddef.h>
 
+#include "../../include/fa_probe.h"
+
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -66,7 +68,8 @@ __global__ void __launch_bounds__(256) update_kernel(float* __restrict__ buf, si
 // hipError_t value (invalid mode or size: hipErrorInvalidValue).  The grid
 // is 8 workgroups of 256 lanes per compute unit, so the launch does not
 // depend on n beyond the loop count.
-extern "C" int fa_probe_update(int mode, float* buf, size_t n, int passes, hipStream_t stream) {
+extern "C" int fa_probe_update(int mode, float* buf, size_t n, int passes, void* stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (buf == nullptr || n == 0 || passes < 1 || mode < 0 || mode > 2)
     return (int)hipErrorInvalidValue;
   int dev = 0, cus = 0;
@@ -90,7 +93,8 @@ extern "C" int fa_probe_update(int mode, float* buf, size_t n, int passes, hipSt
 // wave 4 x `iters` dense bf16 MFMAs of 32x32x16 (32768 flops each).  `out`
 // holds blocks x 256 floats (one per lane).  Returns 0 or a hipError_t value
 // (bad arguments: hipErrorInvalidValue, before any HIP call).
-extern "C" int fa_probe_mfma(float* out, int blocks, int iters, hipStream_t stream) {
+extern "C" int fa_probe_mfma(float* out, int blocks, int iters, void* stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (out == nullptr || blocks < 1 || iters < 1) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(mfma_kernel, dim3(blocks), dim3(256), 0, stream, out, iters);
   return (int)hipGetLastError();

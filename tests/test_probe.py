@@ -1,9 +1,10 @@
-"""The update-rate probe library (measurement support beside libfa.so): it
-exports its entry point, rejects bad arguments before any HIP call, and on
-the GPU its atomic and read-modify-write passes add exactly once per
-element per pass."""
+"""The probe library (measurement support beside libfa.so): it exports the
+entry points include/fa_probe.h declares, rejects bad arguments before any
+HIP call, and on the GPU its atomic and read-modify-write passes add
+exactly once per element per pass."""
 import ctypes
 import os
+import re
 import subprocess
 
 import pytest
@@ -24,10 +25,25 @@ def _lib():
     return lib
 
 
-def test_probe_exports_its_entry_point():
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "fa_probe.h")
+
+
+def test_probe_exports_every_declared_entry_point():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    declared = set(re.findall(r"\b(fa_probe_[a-z0-9_]+)\s*\(", text))
+    assert declared == {"fa_probe_update", "fa_probe_mfma"}
     out = subprocess.run(["nm", "-D", "--defined-only", build.PROBE_LIB], capture_output=True,
                          text=True, check=True).stdout
-    assert "fa_probe_update" in {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert declared <= {line.split()[-1] for line in out.splitlines() if line.strip()}
+
+
+@pytest.mark.parametrize("out,blocks,iters", [(None, 1, 1), (256, 0, 1), (256, 1, 0)])
+def test_mfma_probe_rejects_bad_arguments(out, blocks, iters):
+    lib = _lib()
+    lib.fa_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_probe_mfma.restype = ctypes.c_int
+    assert lib.fa_probe_mfma(out, blocks, iters, None) == HIP_ERROR_INVALID_VALUE
 
 
 @pytest.mark.parametrize("mode,buf,n,passes", [(3, 256, 64, 1), (-1, 256, 64, 1),
