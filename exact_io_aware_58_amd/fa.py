@@ -257,3 +257,42 @@ def backward(q, k, v, o, do, lse, scale, causal=False, dq=None, dk=None, dv=None
     if rc != FA_OK:
         raise FAError(rc, "fa_bwd")
     return dq, dk, dv
+
+
+_attention_fn = None
+
+
+def _attention_function():
+    """The torch.autograd.Function behind attention(), built on first use
+    (torch is imported lazily, like everywhere in this module)."""
+    global _attention_fn
+    if _attention_fn is None:
+        import torch
+
+        class _Attention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, scale, causal):
+                o, lse = forward(q, k, v, scale, causal)
+                ctx.save_for_backward(q, k, v, o, lse)
+                ctx.scale, ctx.causal = scale, causal
+                return o
+
+            @staticmethod
+            def backward(ctx, do):
+                q, k, v, o, lse = ctx.saved_tensors
+                dq, dk, dv = backward(q, k, v, o, do.contiguous(), lse, ctx.scale, ctx.causal)
+                return dq, dk, dv, None, None
+
+        _attention_fn = _Attention
+    return _attention_fn
+
+
+def attention(q, k, v, scale=None, causal=False):
+    """O = softmax(scale Q K^T) V for (B, H, N, D) contiguous device tensors,
+    differentiable through torch autograd: the forward runs fa_fwd and keeps
+    Q, K, V, O and LSE; the backward runs fa_bwd on the incoming dO (16-bit
+    dtypes; the fp32 path is forward only).  scale defaults to 1/sqrt(D)."""
+    if scale is None:
+        scale = q.shape[-1] ** -0.5
+    return _attention_function().apply(q, k, v, float(scale), bool(causal))
+
