@@ -65,6 +65,41 @@ def test_random_forward_backward(i):
     assert max(eq, ek, ev) <= tol["grad_rel"]
 
 
+def _wide_case(i):
+    r = np.random.default_rng([2026, i])
+    B = int(r.integers(1, 3))
+    H = int(r.integers(260, 521)) // B
+    N = int(r.integers(260, 641))
+    D = int(r.choice([64, 128]))
+    causal = bool(r.integers(0, 2))
+    dtype = str(r.choice(["bf16", "f16"]))
+    scale = float(r.uniform(0.5, 2.0) / np.sqrt(D))
+    return B, H, N, D, causal, dtype, scale
+
+
+@pytest.mark.parametrize("i", range(4))
+def test_random_many_heads(i):
+    """As test_random_forward_backward, on grids of 260-520 (batch, head)
+    pairs: the forward takes the ping-pong kernel and the D = 64 backward
+    the separate dK/dV and dQ kernels (the small random cases above take the
+    4-wave forward and the combined backward launch)."""
+    B, H, N, D, causal, dtype, scale = _wide_case(i)
+    say(f"[random wide {i}] B={B} H={H} N={N} D={D} causal={causal} {dtype} scale={scale:.4f}")
+    shape = (B, H, N, D)
+    vals, devs = _draw(6000 + i, {n: shape for n in ("q", "k", "v", "do")}, dtype)
+    o, lse = fa.forward(devs["q"], devs["k"], devs["v"], scale, causal)
+    dq, dk, dv = fa.backward(devs["q"], devs["k"], devs["v"], o, devs["do"], lse, scale, causal)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_fwd(vals["q"], vals["k"], vals["v"], scale, causal)
+    rq, rk, rv = oracle.attention_bwd(vals["q"], vals["k"], vals["v"], vals["do"], scale, causal)
+    tol = TOL[dtype]
+    eo, el = max_abs(to_f64(o), ro), max_abs(to_f64(lse), rl)
+    eq, ek, ev = rel_to_max(to_f64(dq), rq), rel_to_max(to_f64(dk), rk), rel_to_max(to_f64(dv), rv)
+    say(f"    O {eo:.2e} LSE {el:.2e} dQ/dK/dV rel {eq:.2e}/{ek:.2e}/{ev:.2e}")
+    assert eo <= tol["o"] and el <= tol["lse"]
+    assert max(eq, ek, ev) <= tol["grad_rel"]
+
+
 @pytest.mark.parametrize("i", range(8))
 def test_random_partial(i):
     """Partial attention of a query block over a key block at random
