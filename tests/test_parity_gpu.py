@@ -117,6 +117,55 @@ def test_fp16_weight_near_the_rescale_bound(causal, D, heads):
     assert eo <= TOL["f16"]["o"] and el <= TOL["f16"]["lse"]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("mult", [None, 2.0 ** -10, 8.0, 64.0],
+                         ids=["scale2^-32", "scale2^-10", "scale8", "scale64"])
+def test_extreme_scales(mult, causal, D, dtype):
+    """scale = mult/sqrt(D), from the smallest scale the ABI accepts (2^-32:
+    every weight is 1 to fp32 precision, so O is the mean of the visible
+    values) to 64/sqrt(D) (scores spread over hundreds of log units: nearly
+    one-hot rows, and the lazily kept reference maximum moves often);
+    forward and, for 16-bit types, backward against the oracle.
+
+    Two tolerances follow the arithmetic rather than the defaults.  fp32:
+    a score's rounding error grows with its terms, up to D * 2^-24 *
+    scale * sum_d |q_d k_d| (recursive summation over d), which at scale
+    64/sqrt(D) is far above 1e-5; LSE may move by that much and O by twice
+    that times max|V|.  fp16 gradients: dQ and dK are scale times O(1), below
+    fp16's smallest subnormal at scale 2^-32, so the reference is the
+    oracle's value rounded to fp16 (zero there): the best the output can
+    hold."""
+    scale = 2.0 ** -32 if mult is None else mult / np.sqrt(D)
+    say(f"[extreme scale] scale={scale:g} D={D} causal={causal} dtype={dtype}")
+    shape = (1, 2, 300, D)
+    grad = dtype != "f32"
+    vals, devs = draw_case(900 + D + causal, shape, dtype, grad=grad)
+    o, lse = _fwd(devs, scale, causal)
+    ro, rl = oracle.attention_fwd(vals["q"], vals["k"], vals["v"], scale, causal)
+    tol = TOL[dtype]
+    tol_o, tol_l = tol["o"], tol["lse"]
+    if dtype == "f32":
+        terms = np.einsum("bhid,bhjd->bhij", np.abs(vals["q"]), np.abs(vals["k"]))
+        bound = D * 2.0 ** -24 * scale * float(terms.max())
+        tol_o += 2 * bound * float(np.abs(vals["v"]).max())
+        tol_l += bound
+    eo, el = max_abs(to_f64(o), ro), max_abs(to_f64(lse), rl)
+    say(f"    O {eo:.2e} LSE {el:.2e} (tolerances {tol_o:.2e}, {tol_l:.2e})")
+    assert eo <= tol_o and el <= tol_l
+    if not grad:
+        return
+    dq, dk, dv = fa.backward(devs["q"], devs["k"], devs["v"], o, devs["do"], lse, scale, causal)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_bwd(vals["q"], vals["k"], vals["v"], vals["do"], scale, causal)
+    if dtype == "f16":
+        rq, rk, rv = (r.astype(np.float16).astype(np.float64) for r in (rq, rk, rv))
+    eq, ek, ev = rel_to_max(to_f64(dq), rq), rel_to_max(to_f64(dk), rk), rel_to_max(to_f64(dv), rv)
+    say(f"    rel-to-max dQ={eq:.2e} dK={ek:.2e} dV={ev:.2e}")
+    assert max(eq, ek, ev) <= tol["grad_rel"]
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
