@@ -289,6 +289,31 @@ def test_forward_and_backward_are_repeatable():
         assert torch.equal(a, b)
 
 
+def test_side_stream_gives_the_same_bits():
+    """The stream argument: forward, backward and partial attention enqueued
+    on a non-default stream (the binding passes torch's current stream)
+    produce the bits of the default-stream run, with the inputs written on
+    the default stream first and an event ordering the two."""
+    vals, devs = draw_case(4321, (2, 3, 500, 128), "bf16", grad=True)
+
+    def run():
+        o, lse = fa.forward(devs["q"], devs["k"], devs["v"], 0.09, True)
+        g = fa.backward(devs["q"], devs["k"], devs["v"], o, devs["do"], lse, 0.09, True)
+        op, lp = fa.forward_partial(devs["q"], devs["k"], devs["v"], 0.09, True, 100, 0)
+        return [o, lse, *g, op, lp]
+
+    ref = [t.clone() for t in run()]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+
+
 # ------------------------------------------------------------ five workloads
 
 def _workload_devs(w):
