@@ -314,6 +314,49 @@ def test_side_stream_gives_the_same_bits():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_graph_capture_replays_match_eager(D):
+    """A training step's forward and backward captured into a HIP graph
+    (torch.cuda.CUDAGraph; the library only launches kernels, no memset or
+    allocation) and replayed three times, new input values written eagerly
+    between replays: every replay equals the eager run on the same values,
+    bit for bit."""
+    B, H, N, scale = 1, 4, 700, D ** -0.5
+    draws = [draw_case(7000 + 10 * r + D, (B, H, N, D), "bf16", grad=True)[1] for r in range(4)]
+    q, k, v, do = (draws[0][n].clone() for n in ("q", "k", "v", "do"))
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(fa.workspace_bytes(q, True), 16), dtype=torch.uint8, device=q.device)
+
+    def step():
+        fa.forward(q, k, v, scale, True, out=o, lse=lse)
+        fa.backward(q, k, v, o, do, lse, scale, True, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the capture
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for r in range(1, 4):
+        for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
+            t.copy_(draws[r][name])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (o, lse, dq, dk, dv)]
+        eo, el = fa.forward(draws[r]["q"], draws[r]["k"], draws[r]["v"], scale, True)
+        eg = fa.backward(draws[r]["q"], draws[r]["k"], draws[r]["v"], eo, draws[r]["do"], el,
+                         scale, True)
+        torch.cuda.synchronize()
+        for a, b in zip(got, [eo, el, *eg]):
+            assert torch.equal(a, b)
+
+
 # ------------------------------------------------------------ five workloads
 
 def _workload_devs(w):
